@@ -1,0 +1,175 @@
+/*
+ * pagedkv — single-query attention over a block-paged KV cache on MI355X
+ * (gfx950), plus the two paging helpers it needs: slot-mapped append of new
+ * tokens and block-granular copy-on-write.
+ *
+ * C ABI: plain pointers and sizes.  Every pointer named "device" must point
+ * to memory on the current HIP device; "host" pointers are read before the
+ * call returns.  Every entry point is asynchronous on the given stream
+ * (a hipStream_t passed as void*, NULL for the null stream): it performs no
+ * device allocation and no host/device synchronisation, and the caller owns
+ * every buffer and keeps it alive until the stream has passed the call.
+ *
+ * All argument checks run on the host before any HIP call, so a bad call
+ * returns its status code and touches neither the device nor the stream.
+ * Device-side contract violations (a block id outside [0, num_blocks), a
+ * context_lens entry above max_context_len) are not reported: the kernels
+ * clamp or skip them so that no access leaves the buffers (a context is
+ * clamped to max_context_len), and the results for the affected rows are
+ * unspecified.
+ *
+ * Sources: "PagedAttention" (e-fortepiano.pl, Catalan encyclopedia
+ * article), sections "Descripció" and "Formulació matemàtica"; "Atención
+ * paginada en modelos de lenguaje grandes (LLM)" (7minutos.es), the
+ * PagePool / PagedRequest part and the prefix-sharing (copy-on-write) part.
+ *
+ * Layouts (all row-major, fp16 = IEEE binary16):
+ *   q, out          [B][H][D]
+ *   k_pool, v_pool  [num_blocks][H][D/8][16][8]: one physical block holds
+ *                   16 tokens for every head; inside the tile of one
+ *                   (block, head) the head dimension is split into D/8
+ *                   groups of 8 consecutive values and each group stores its
+ *                   8 values for token 0, token 1, ..., token 15 in turn.
+ *                   Value d of head h for the token at position p of block n
+ *                   is element ((n*H + h)*(D/8) + d/8)*128 + p*8 + d%8.
+ *   block_tables    [B][max_blocks_per_seq] int32: logical block j of
+ *                   sequence b lives in physical block block_tables[b][j];
+ *                   entries past the sequence's last block are ignored.
+ *   context_lens    [B] int32: tokens of sequence b that its query attends
+ *                   to (positions 0 .. context_lens[b]-1, the query's own
+ *                   token included once it has been appended).
+ *   slot_mapping    [T] int32: slot = physical_block*16 + position; a
+ *                   negative slot skips that row.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
+  PKV_ERR_BAD_SHAPE = 2,           /* negative or zero size where one is needed,
+                                      D not 64/128, table narrower than the context */
+  PKV_ERR_MISALIGNED = 3,          /* a data pointer is not 16-byte aligned
+                                      (int32 arrays: 4-byte) */
+  PKV_ERR_UNSUPPORTED = 4,         /* block_size other than 16 */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the required size */
+  PKV_ERR_HIP = 6                  /* the HIP runtime reported a launch error */
+};
+
+/* Tokens per physical block ("Atención paginada ...", 7minutos.es,
+ * PagePool part: pages of 16 tokens). */
+#define PKV_BLOCK_TOKENS 16
+
+/*
+ * Bytes of device workspace pkv_pa_decode needs for this shape (0 when every
+ * sequence fits in one partition).  Pure host function; max_context_len is
+ * the largest entry of context_lens the caller will pass.  Returns 0 for
+ * invalid sizes.
+ */
+size_t pkv_pa_decode_workspace_size(int32_t B, int32_t H, int32_t D,
+                                    int32_t max_context_len);
+
+/*
+ * PagedAttention decode ("PagedAttention", e-fortepiano.pl, "Formulació
+ * matemàtica" and "Descripció"): for every sequence b and head h,
+ *
+ *   out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) * V_t,
+ *
+ * over t = 0 .. context_lens[b]-1, where K_t / V_t are read from physical
+ * block block_tables[b][t/16] at position t%16 of k_pool / v_pool.  The
+ * result is computed block by block in fp32 with an online softmax and,
+ * for long contexts, split into partitions whose partial results are merged
+ * in ascending partition order; it is rounded to fp16 (round to nearest
+ * even).  A sequence with context 0 gets a zero row.  The arithmetic order
+ * depends only on logical positions, so moving blocks to other physical ids
+ * or sharing them between sequences does not change any output bit.
+ *
+ * device: q, k_pool, v_pool, out (16-byte aligned), block_tables,
+ *         context_lens, workspace (256-byte aligned, may be NULL when the
+ *         required size is 0).
+ * host:   sizes, scale; max_context_len >= every context_lens[b] chooses the
+ *         partitioning; block_size must be 16; max_blocks_per_seq*16 must be
+ *         >= max_context_len.
+ */
+int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t max_context_len,
+                  int32_t B, int32_t H, int32_t D, int32_t block_size,
+                  int32_t num_blocks, float scale, void* out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_pa_decode with an explicit partition length in tokens (a positive
+ * multiple of 16, at most 512), or 0 for the default choice.  The workspace
+ * size for it is pkv_pa_decode_workspace_size_ex with the same value.
+ */
+int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len,
+                     int32_t B, int32_t H, int32_t D, int32_t block_size,
+                     int32_t num_blocks, float scale, void* out,
+                     void* workspace, size_t workspace_bytes,
+                     int32_t partition_tokens, void* stream);
+
+size_t pkv_pa_decode_workspace_size_ex(int32_t B, int32_t H, int32_t D,
+                                       int32_t max_context_len,
+                                       int32_t partition_tokens);
+
+/* Partition length in tokens that pkv_pa_decode picks for this shape. */
+int32_t pkv_pa_decode_default_partition(int32_t B, int32_t H, int32_t D,
+                                        int32_t max_context_len);
+
+/*
+ * Slot-mapped append of new tokens into one layer's pools ("Atención
+ * paginada ...", 7minutos.es, PagePool / PagedRequest part: each generated
+ * token is stored in the page its block table names).  For every row t
+ * with slot_mapping[t] >= 0, k[t] and v[t] ([H][D] fp16 each) are copied
+ * bit for bit into position slot%16 of block slot/16.  Rows with a
+ * negative slot or a block >= num_blocks are skipped.  Two rows with the
+ * same slot are a caller error (which one lands is unspecified).
+ *
+ * device: k, v ([T][H][D], 16-byte aligned), slot_mapping, k_pool, v_pool.
+ */
+int pkv_kv_append(const void* k, const void* v, const int32_t* slot_mapping,
+                  int32_t T, void* k_pool, void* v_pool, int32_t num_blocks,
+                  int32_t H, int32_t D, int32_t block_size, void* stream);
+
+/*
+ * Block-granular copy-on-write ("Atención paginada ...", 7minutos.es,
+ * prefix-sharing part; "PagedAttention", e-fortepiano.pl, "Descripció"):
+ * for every pair (src, dst) in src_dst_pairs and every layer l, the whole
+ * physical block dst of k_pools[l] and of v_pools[l] becomes a bit copy of
+ * block src.  Reference counts live with the caller.  Pairs must be
+ * conflict-free (no dst repeated, no dst that is also a src); pairs with an
+ * id outside [0, num_blocks) are skipped.
+ *
+ * host:   k_pools, v_pools: arrays of num_layers device pointers (16-byte
+ *         aligned), read before the call returns.
+ * device: src_dst_pairs [n_pairs][2] int32.
+ * block_bytes: bytes of one block of one pool (H*16*D*2 for fp16), a
+ *         positive multiple of 16.
+ */
+int pkv_cow_copy_blocks(void* const* k_pools, void* const* v_pools,
+                        int32_t num_layers, const int32_t* src_dst_pairs,
+                        int32_t n_pairs, int32_t num_blocks, int64_t block_bytes,
+                        void* stream);
+
+/* Static description of a status code. */
+const char* pkv_status_string(int code);
+
+/* Library ABI version (increments when a signature changes). */
+int32_t pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,16 @@
+"""PagedAttention decode on MI355X (gfx950).
+
+Single-query attention over a KV cache cut into 16-token blocks scattered
+across a physical block pool and reached through per-sequence block tables,
+plus the two paging helpers: slot-mapped append and block copy-on-write.
+The compute runs in hand-written HIP kernels behind the C ABI of
+``libpagedkv.so`` (include/pagedkv.h); ``ops`` marshals torch tensors to it,
+``blocks`` is the host-side block manager that produces tables, slots and
+copy pairs.
+"""
+
+from ._lib import LIB_PATH, LibraryMissing, PagedKVError, load_library  # noqa: F401
+from .blocks import (PAGE_TOKENS, PagedRequest, PagePool, PoolExhausted,  # noqa: F401
+                     device_arrays, kv_bytes_per_token)
+from .ops import (cow_copy_blocks, default_partition, kv_append, pa_decode,  # noqa: F401
+                  pa_decode_workspace_size, pool_shape)

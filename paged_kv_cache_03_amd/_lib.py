@@ -1,0 +1,84 @@
+"""ctypes loader for libpagedkv.so (the C ABI declared in include/pagedkv.h).
+
+There is no fallback: if the library has not been built, every call that
+needs it raises ``LibraryMissing``.
+"""
+
+import ctypes
+import os
+import threading
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_DIR, "libpagedkv.so")
+ABI_VERSION = 1
+
+# Status codes (enum pkv_status)
+OK = 0
+ERR_NULL_PTR = 1
+ERR_BAD_SHAPE = 2
+ERR_MISALIGNED = 3
+ERR_UNSUPPORTED = 4
+ERR_WORKSPACE_TOO_SMALL = 5
+ERR_HIP = 6
+
+# Every symbol include/pagedkv.h declares, with its ctypes signature.
+_c = ctypes
+_vp = _c.c_void_p
+_i32 = _c.c_int32
+_i32p = _c.c_void_p  # int32_t* passed as an address
+SIGNATURES = {
+    "pkv_pa_decode_workspace_size": (_c.c_size_t, [_i32, _i32, _i32, _i32]),
+    "pkv_pa_decode_workspace_size_ex": (_c.c_size_t, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32]),
+    "pkv_pa_decode": (_c.c_int, [_vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _c.c_float, _vp, _vp, _c.c_size_t, _vp]),
+    "pkv_pa_decode_ex": (_c.c_int, [_vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _c.c_float, _vp, _vp, _c.c_size_t, _i32, _vp]),
+    "pkv_kv_append": (_c.c_int, [_vp, _vp, _i32p, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_cow_copy_blocks": (_c.c_int, [_c.POINTER(_vp), _c.POINTER(_vp), _i32, _i32p, _i32, _i32,
+                                       _c.c_int64, _vp]),
+    "pkv_status_string": (_c.c_char_p, [_c.c_int]),
+    "pkv_abi_version": (_i32, []),
+}
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, func, code, text):
+        super().__init__(f"{func} failed: status {code} ({text})")
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and type the shared library; raise LibraryMissing if it is
+    not there."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise LibraryMissing(
+                f"{path} is not built; run `python -m paged_kv_cache_03_amd.build` "
+                "(hipcc for gfx950) first")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.pkv_abi_version() != ABI_VERSION:
+            raise LibraryMissing(f"{path} has ABI {lib.pkv_abi_version()}, expected {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def check(func, code):
+    if code != OK:
+        text = load_library().pkv_status_string(code).decode()
+        raise PagedKVError(func, code, text)

@@ -1,0 +1,218 @@
+// C ABI of libpagedkv: argument checks (all on the host, before any HIP
+// call), partition choice, workspace sizing and launches.  Declarations and
+// the contract of every entry point are in include/pagedkv.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "pagedkv.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kBlockTokens = PKV_BLOCK_TOKENS;
+constexpr size_t kWsAlign = 256;
+// Enough workgroups to keep all 256 CUs busy several times over.
+constexpr long long kTargetWorkgroups = 2048;
+constexpr int kDefaultMaxPartitionTokens = 256;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int waves_per_group(int32_t H) { return (H % 4 == 0) ? 4 : (H % 2 == 0) ? 2 : 1; }
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+// Largest partition (<= 256 tokens) that still gives enough workgroups for
+// the longest context; short batches are split finer so they fill the GPU.
+int32_t choose_partition(int32_t B, int32_t H, int32_t max_ctx) {
+  const long long groups = (long long)B * (H / waves_per_group(H));
+  int32_t part = kDefaultMaxPartitionTokens;
+  while (part > kBlockTokens && groups * ceil_div(max_ctx, part) < kTargetWorkgroups) part /= 2;
+  return part;
+}
+
+bool partition_ok(int32_t part) {
+  return part == 0 || (part > 0 && part % kBlockTokens == 0 &&
+                       part <= pkv::kMaxPartitionBlocks * kBlockTokens);
+}
+
+struct WsLayout {
+  int32_t max_parts = 0;
+  size_t ml_bytes = 0;
+  size_t total = 0;
+};
+
+WsLayout ws_layout(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t part) {
+  WsLayout w;
+  w.max_parts = max_ctx > 0 ? ceil_div(max_ctx, part) : 0;
+  if (w.max_parts <= 1) return w;
+  const size_t rows = (size_t)B * H * w.max_parts;
+  w.ml_bytes = round_up(rows * 2 * sizeof(float), kWsAlign);
+  w.total = w.ml_bytes + rows * D * sizeof(float);
+  return w;
+}
+
+bool decode_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx) {
+  return B >= 0 && H > 0 && head_dim_ok(D) && max_ctx >= 0 && max_ctx <= (1 << 24) &&
+         (long long)B * H <= (1LL << 26);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return kAbiVersion; }
+
+const char* pkv_status_string(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL_PTR: return "a required pointer is NULL";
+    case PKV_ERR_BAD_SHAPE: return "invalid size or shape";
+    case PKV_ERR_MISALIGNED: return "pointer not aligned (16 bytes for data, 4 for int32 arrays, 256 for workspace)";
+    case PKV_ERR_UNSUPPORTED: return "unsupported block size (only 16 tokens per block)";
+    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than pkv_pa_decode_workspace_size";
+    case PKV_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t pkv_pa_decode_default_partition(int32_t B, int32_t H, int32_t D, int32_t max_context_len) {
+  if (!decode_shape_ok(B, H, D, max_context_len)) return 0;
+  return choose_partition(B, H, max_context_len);
+}
+
+size_t pkv_pa_decode_workspace_size_ex(int32_t B, int32_t H, int32_t D, int32_t max_context_len,
+                                       int32_t partition_tokens) {
+  if (!decode_shape_ok(B, H, D, max_context_len) || !partition_ok(partition_tokens)) return 0;
+  const int32_t part = partition_tokens ? partition_tokens : choose_partition(B, H, max_context_len);
+  return ws_layout(B, H, D, max_context_len, part).total;
+}
+
+size_t pkv_pa_decode_workspace_size(int32_t B, int32_t H, int32_t D, int32_t max_context_len) {
+  return pkv_pa_decode_workspace_size_ex(B, H, D, max_context_len, 0);
+}
+
+int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
+                     int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                     void* stream) {
+  if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
+  if (!decode_shape_ok(B, H, D, max_context_len) || !partition_ok(partition_tokens))
+    return PKV_ERR_BAD_SHAPE;
+  if (B == 0) return PKV_OK;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      (long long)max_blocks_per_seq * kBlockTokens < max_context_len)
+    return PKV_ERR_BAD_SHAPE;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PKV_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_MISALIGNED;
+
+  const int32_t part = partition_tokens ? partition_tokens : choose_partition(B, H, max_context_len);
+  const WsLayout ws = ws_layout(B, H, D, max_context_len, part);
+  if (ws.total > 0) {
+    if (!workspace) return PKV_ERR_NULL_PTR;
+    if (!aligned(workspace, kWsAlign)) return PKV_ERR_MISALIGNED;
+    if (workspace_bytes < ws.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const int wpg = waves_per_group(H);
+  const long long grid = (long long)B * (H / wpg) * (ws.max_parts > 0 ? ws.max_parts : 1);
+  if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
+
+  pkv::PartArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = static_cast<_Float16*>(out);
+  a.ws_ml = ws.total ? static_cast<float*>(workspace) : nullptr;
+  a.ws_acc = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_bytes) : nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.B = B;
+  a.H = H;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_limit = max_context_len;
+  a.num_blocks = num_blocks;
+  a.part_blocks = part / kBlockTokens;
+  a.max_parts = ws.max_parts;
+  a.head_groups = H / wpg;
+  a.waves_per_group = wpg;
+  const hipError_t e = pkv::launch_pa_decode(a, D, (int)grid, wpg * 64,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
+                  int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return pkv_pa_decode_ex(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                          max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
+                          workspace_bytes, 0, stream);
+}
+
+int pkv_kv_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,
+                  void* k_pool, void* v_pool, int32_t num_blocks, int32_t H, int32_t D,
+                  int32_t block_size, void* stream) {
+  if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
+  if (T < 0 || H <= 0 || !head_dim_ok(D) || num_blocks <= 0) return PKV_ERR_BAD_SHAPE;
+  if (T == 0) return PKV_OK;
+  if ((long long)T * H * (D / 8) >= (1LL << 31) * 256LL) return PKV_ERR_BAD_SHAPE;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_NULL_PTR;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 4))
+    return PKV_ERR_MISALIGNED;
+  pkv::AppendArgs a;
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.T = T;
+  a.H = H;
+  a.D = D;
+  a.num_blocks = num_blocks;
+  const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_cow_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                        const int32_t* src_dst_pairs, int32_t n_pairs, int32_t num_blocks,
+                        int64_t block_bytes, void* stream) {
+  if (num_layers <= 0 || n_pairs < 0 || num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16)
+    return PKV_ERR_BAD_SHAPE;
+  if (n_pairs == 0) return PKV_OK;
+  if ((long long)n_pairs * 2 * pkv::kMaxCowLayers >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
+  if (!k_pools || !v_pools || !src_dst_pairs) return PKV_ERR_NULL_PTR;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    if (!k_pools[l] || !v_pools[l]) return PKV_ERR_NULL_PTR;
+    if (!aligned(k_pools[l], 16) || !aligned(v_pools[l], 16)) return PKV_ERR_MISALIGNED;
+  }
+  if (!aligned(src_dst_pairs, 4)) return PKV_ERR_MISALIGNED;
+  for (int32_t l0 = 0; l0 < num_layers; l0 += pkv::kMaxCowLayers) {
+    pkv::CowArgs a;
+    memset(&a, 0, sizeof(a));
+    a.layers = num_layers - l0 < pkv::kMaxCowLayers ? num_layers - l0 : pkv::kMaxCowLayers;
+    for (int i = 0; i < a.layers; ++i) {
+      a.k[i] = k_pools[l0 + i];
+      a.v[i] = v_pools[l0 + i];
+    }
+    a.pairs = src_dst_pairs;
+    a.block_bytes = block_bytes;
+    a.n_pairs = n_pairs;
+    a.num_blocks = num_blocks;
+    const hipError_t e = pkv::launch_cow_copy(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Longest partition a decode workgroup handles, in blocks (512 tokens).
+constexpr int kMaxPartitionBlocks = 32;
+
+struct PartArgs {
+  const _Float16* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  _Float16* out;
+  float* ws_ml;        // [B][H][max_parts][2]: running max (log2 units), running sum
+  float* ws_acc;       // [B][H][max_parts][D]: unnormalised weighted sums
+  float scale_log2;    // scale * log2(e)
+  int B, H;
+  int max_blocks;      // table row length
+  int ctx_limit;       // contexts are clamped to this (host's max_context_len)
+  int num_blocks;
+  int part_blocks;     // partition length in blocks
+  int max_parts;       // partitions of the longest sequence
+  int head_groups;     // H / waves_per_group
+  int waves_per_group;
+};
+
+struct MergeArgs {
+  const float* ws_ml;
+  const float* ws_acc;
+  const int32_t* context_lens;
+  _Float16* out;
+  int B, H;
+  int ctx_limit;
+  int part_blocks;
+  int max_parts;
+};
+
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+  void* k_pool;
+  void* v_pool;
+  int T, H, D;
+  int num_blocks;
+};
+
+constexpr int kMaxCowLayers = 32;  // per launch; more layers take more launches
+
+struct CowArgs {
+  void* k[kMaxCowLayers];
+  void* v[kMaxCowLayers];
+  const int32_t* pairs;
+  long long block_bytes;
+  int n_pairs;
+  int layers;
+  int num_blocks;
+};
+
+hipError_t launch_pa_decode(const PartArgs& part, int D, int grid_part, int threads,
+                            hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_cow_copy(const CowArgs& a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,160 @@
+"""torch-facing wrappers over the C ABI: argument marshalling only.
+
+Tensors must be on one HIP device and contiguous; every call is enqueued on
+that device's current torch stream and returns without synchronising.  All
+arithmetic happens in the HIP kernels of libpagedkv.so.
+
+Pool layout (both K and V, per layer): ``[num_blocks][H][D/8][16][8]``
+fp16; ``pool_shape`` gives it.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+BLOCK_TOKENS = 16
+
+
+def pool_shape(num_blocks, num_heads, head_dim):
+    return (num_blocks, num_heads, head_dim // 8, BLOCK_TOKENS, 8)
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _pool_blocks(pool, name, H, D, device):
+    _need(pool, name, torch.float16, device)
+    per_block = H * BLOCK_TOKENS * D
+    if pool.numel() % per_block:
+        raise ValueError(f"{name} is not a whole number of [H][D/8][16][8] blocks")
+    return pool.numel() // per_block
+
+
+def pa_decode_workspace_size(batch, num_heads, head_dim, max_context_len, partition_tokens=0):
+    lib = _lib.load_library()
+    return int(lib.pkv_pa_decode_workspace_size_ex(batch, num_heads, head_dim,
+                                                   max_context_len, partition_tokens))
+
+
+def default_partition(batch, num_heads, head_dim, max_context_len):
+    return int(_lib.load_library().pkv_pa_decode_default_partition(
+        batch, num_heads, head_dim, max_context_len))
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
+              max_context_len=None, workspace=None, partition_tokens=0):
+    """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the first
+    context_lens[b] tokens of sequence b, read through block_tables[b].
+
+    q: [B][H][D] fp16; pools: [NB][H][D/8][16][8] fp16; block_tables:
+    [B][max_blocks] int32; context_lens: [B] int32.  ``max_context_len`` must
+    be >= every context length; when omitted it is read back from the device
+    (one synchronisation).  ``workspace``: a uint8 device tensor of at least
+    ``pa_decode_workspace_size(...)`` bytes, allocated here when omitted."""
+    lib = _lib.load_library()
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    B, H, D = q.shape
+    NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
+    if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
+        raise ValueError("k_pool and v_pool differ in size")
+    _need(block_tables, "block_tables", torch.int32, dev, ndim=2)
+    _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens do not match the batch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, dev, ndim=3)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B][H][D]")
+    need = pa_decode_workspace_size(B, H, D, max_context_len, partition_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+        ws_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        code = lib.pkv_pa_decode_ex(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), max_context_len, B, H, D, BLOCK_TOKENS, NB, float(scale),
+            _ptr(out), _ptr(workspace), ws_bytes, partition_tokens, _stream_handle(dev))
+    _lib.check("pkv_pa_decode", code)
+    return out
+
+
+def kv_append(k, v, slot_mapping, k_pool, v_pool):
+    """Write row t of k / v ([T][H][D] fp16) into slot slot_mapping[t]
+    (block slot//16, position slot%16) of one layer's pools; negative slots
+    are skipped."""
+    lib = _lib.load_library()
+    _need(k, "k", torch.float16, ndim=3)
+    dev = k.device
+    _need(v, "v", torch.float16, dev, ndim=3)
+    if v.shape != k.shape:
+        raise ValueError("k and v differ in shape")
+    T, H, D = k.shape
+    _need(slot_mapping, "slot_mapping", torch.int32, dev, ndim=1)
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per row")
+    NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
+    if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
+        raise ValueError("k_pool and v_pool differ in size")
+    with torch.cuda.device(dev):
+        code = lib.pkv_kv_append(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_pool),
+                                 _ptr(v_pool), NB, H, D, BLOCK_TOKENS, _stream_handle(dev))
+    _lib.check("pkv_kv_append", code)
+
+
+def cow_copy_blocks(src_dst_pairs, k_pools, v_pools):
+    """For every (src, dst) row of ``src_dst_pairs`` ([n][2] int32, device)
+    copy physical block src over block dst in every layer's K and V pool
+    (lists of equally shaped fp16 pools)."""
+    lib = _lib.load_library()
+    k_pools = list(k_pools)
+    v_pools = list(v_pools)
+    if not k_pools or len(k_pools) != len(v_pools):
+        raise ValueError("need one K and one V pool per layer")
+    dev = k_pools[0].device
+    _need(src_dst_pairs, "src_dst_pairs", torch.int32, dev, ndim=2)
+    if src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n][2]")
+    first = k_pools[0]
+    for i, p in enumerate(k_pools + v_pools):
+        _need(p, f"pool {i}", torch.float16, dev)
+        if p.shape != first.shape:
+            raise ValueError("all pools must have the same shape")
+    NB = first.shape[0]
+    block_bytes = first[0].numel() * first.element_size()
+    L = len(k_pools)
+    karr = (ctypes.c_void_p * L)(*[p.data_ptr() for p in k_pools])
+    varr = (ctypes.c_void_p * L)(*[p.data_ptr() for p in v_pools])
+    with torch.cuda.device(dev):
+        code = lib.pkv_cow_copy_blocks(karr, varr, L, _ptr(src_dst_pairs),
+                                       src_dst_pairs.shape[0], NB, block_bytes,
+                                       _stream_handle(dev))
+    _lib.check("pkv_cow_copy_blocks", code)

@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and every invalid-argument path returns its status code before any
+HIP call (so no call here can reach a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_03_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libpagedkv.so not built")
+
+A16 = 0x10000        # 16- and 256-byte aligned fake device address (never dereferenced)
+A4 = 0x10004         # only 4-byte aligned
+MIS = 0x10002        # not even 4-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.pkv_status_string(code)
+    assert lib.pkv_status_string(99) == b"unknown status"
+    assert lib.pkv_abi_version() == _lib.ABI_VERSION
+
+
+def decode(lib, **kw):
+    args = dict(q=A16, k=A16, v=A16, tables=A16, maxb=128, ctx=A16, maxctx=2048, B=4, H=32,
+                D=128, bs=16, nb=1024, scale=0.088, out=A16, ws=A16, wsb=1 << 30, part=0)
+    args.update(kw)
+    return lib.pkv_pa_decode_ex(args["q"], args["k"], args["v"], args["tables"], args["maxb"],
+                                args["ctx"], args["maxctx"], args["B"], args["H"], args["D"],
+                                args["bs"], args["nb"], args["scale"], args["out"], args["ws"],
+                                args["wsb"], args["part"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=8), _lib.ERR_UNSUPPORTED),
+    (dict(D=96), _lib.ERR_BAD_SHAPE),
+    (dict(H=0), _lib.ERR_BAD_SHAPE),
+    (dict(B=-1), _lib.ERR_BAD_SHAPE),
+    (dict(maxctx=-5), _lib.ERR_BAD_SHAPE),
+    (dict(maxb=127), _lib.ERR_BAD_SHAPE),          # 127*16 < 2048
+    (dict(nb=0), _lib.ERR_BAD_SHAPE),
+    (dict(part=24), _lib.ERR_BAD_SHAPE),
+    (dict(part=1024), _lib.ERR_BAD_SHAPE),
+    (dict(q=None), _lib.ERR_NULL_PTR),
+    (dict(k=None), _lib.ERR_NULL_PTR),
+    (dict(tables=None), _lib.ERR_NULL_PTR),
+    (dict(out=None), _lib.ERR_NULL_PTR),
+    (dict(q=A4), _lib.ERR_MISALIGNED),
+    (dict(v=A4), _lib.ERR_MISALIGNED),
+    (dict(ctx=MIS), _lib.ERR_MISALIGNED),
+    (dict(ws=None), _lib.ERR_NULL_PTR),
+    (dict(ws=A16 + 16), _lib.ERR_MISALIGNED),
+    (dict(wsb=64), _lib.ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_rejects_bad_arguments(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert decode(lib, B=0, q=None, k=None, v=None, tables=None, ctx=None, out=None) == _lib.OK
+
+
+def test_plain_decode_entry_checks_too(lib):
+    assert lib.pkv_pa_decode(A16, A16, A16, A16, 128, A16, 2048, 4, 32, 128, 8, 1024, 0.1, A16,
+                             A16, 1 << 30, None) == _lib.ERR_UNSUPPORTED
+
+
+def test_workspace_size(lib):
+    B, H, D, ctx = 200, 32, 128, 2048
+    part = lib.pkv_pa_decode_default_partition(B, H, D, ctx)
+    assert part % 16 == 0 and 16 <= part <= 512
+    np_ = -(-ctx // part)
+    rows = B * H * np_
+    ml = -(-rows * 8 // 256) * 256
+    assert lib.pkv_pa_decode_workspace_size(B, H, D, ctx) == ml + rows * D * 4
+    # a context that fits one partition needs no workspace
+    assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, 256, 256) == 0
+    assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, 257, 256) > 0
+    assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, 100, 24) == 0     # invalid partition
+    assert lib.pkv_pa_decode_workspace_size(B, H, 96, 100) == 0           # invalid D
+    # small batches are split finer to fill the GPU
+    assert lib.pkv_pa_decode_default_partition(1, 32, 128, 2048) < part
+
+
+def append(lib, **kw):
+    args = dict(k=A16, v=A16, slots=A16, T=8, kp=A16, vp=A16, nb=64, H=32, D=128, bs=16)
+    args.update(kw)
+    return lib.pkv_kv_append(args["k"], args["v"], args["slots"], args["T"], args["kp"],
+                             args["vp"], args["nb"], args["H"], args["D"], args["bs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=32), _lib.ERR_UNSUPPORTED),
+    (dict(D=80), _lib.ERR_BAD_SHAPE),
+    (dict(T=-1), _lib.ERR_BAD_SHAPE),
+    (dict(nb=0), _lib.ERR_BAD_SHAPE),
+    (dict(slots=None), _lib.ERR_NULL_PTR),
+    (dict(kp=None), _lib.ERR_NULL_PTR),
+    (dict(k=A4), _lib.ERR_MISALIGNED),
+    (dict(vp=A4), _lib.ERR_MISALIGNED),
+    (dict(slots=MIS), _lib.ERR_MISALIGNED),
+])
+def test_append_rejects_bad_arguments(lib, kw, code):
+    assert append(lib, **kw) == code
+
+
+def test_append_nothing_is_a_no_op(lib):
+    assert append(lib, T=0, k=None, v=None, slots=None) == _lib.OK
+
+
+def cow(lib, pools_k, pools_v, layers=2, pairs=A16, n=3, nb=64, bb=131072):
+    K = (ctypes.c_void_p * max(1, len(pools_k)))(*pools_k)
+    V = (ctypes.c_void_p * max(1, len(pools_v)))(*pools_v)
+    return lib.pkv_cow_copy_blocks(K, V, layers, pairs, n, nb, bb, None)
+
+
+def test_cow_rejects_bad_arguments(lib):
+    ok = [A16, A16 + 4096]
+    assert cow(lib, ok, ok, bb=100) == _lib.ERR_BAD_SHAPE
+    assert cow(lib, ok, ok, layers=0) == _lib.ERR_BAD_SHAPE
+    assert cow(lib, ok, ok, nb=0) == _lib.ERR_BAD_SHAPE
+    assert cow(lib, ok, ok, n=-1) == _lib.ERR_BAD_SHAPE
+    assert cow(lib, ok, ok, pairs=None) == _lib.ERR_NULL_PTR
+    assert cow(lib, [A16, None], ok) == _lib.ERR_NULL_PTR
+    assert cow(lib, ok, [A16, A4]) == _lib.ERR_MISALIGNED
+    assert cow(lib, ok, ok, pairs=MIS) == _lib.ERR_MISALIGNED
+    assert cow(lib, ok, ok, n=0, pairs=None) == _lib.OK
+    assert lib.pkv_cow_copy_blocks(None, None, 2, A16, 3, 64, 131072, None) == _lib.ERR_NULL_PTR
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load_library(str(tmp_path / "libpagedkv.so"))

@@ -112,7 +112,9 @@ def tiny(seed=0):
     q = normal_fp16(rng, (len(lens), H, D))
     k_pool = normal_fp16(rng, pool_shape(NB, H, D))
     v_pool = normal_fp16(rng, pool_shape(NB, H, D))
-    return Case("tiny", H, D, NB, lens, tables, q, _scale(D), k_pool, v_pool)
+    case = Case("tiny", H, D, NB, lens, tables, q, _scale(D), k_pool, v_pool)
+    case.meta["seed"] = seed
+    return case
 
 
 def draw_lengths(rng, batch):
@@ -144,6 +146,7 @@ def gpt_batch(batch, seed, num_blocks=None, append=False, heads=32, head_dim=128
     q = normal_fp16(rng, (batch, heads, head_dim))
     case = Case(f"gpt_b{batch}" + ("_append" if append else ""), heads, head_dim,
                 num_blocks, lens, tables, q, _scale(head_dim))
+    case.meta["seed"] = seed
     if fill:
         case.k_pool = normal_fp16(rng, pool_shape(num_blocks, heads, head_dim))
         case.v_pool = normal_fp16(rng, pool_shape(num_blocks, heads, head_dim))
@@ -197,7 +200,7 @@ def shared_prefix(batch=100, seed=3, prefix_tokens=1024, suffix_max=500, heads=3
     q = normal_fp16(rng, (batch, heads, head_dim))
     case = Case(f"shared_prefix_{prefix_tokens}", heads, head_dim, num_blocks, lens,
                 tables, q, _scale(head_dim), cow_pairs=pairs, shared_tables=shared)
-    case.meta.update(prefix_tokens=prefix_tokens, prefix_blocks=pblocks,
+    case.meta.update(seed=seed, prefix_tokens=prefix_tokens, prefix_blocks=pblocks,
                      prefix_ids=prefix_ids.copy(), suffix=suffix)
     if fill:
         case.k_pool = normal_fp16(rng, pool_shape(num_blocks, heads, head_dim))
