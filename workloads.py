@@ -51,7 +51,7 @@ class Case:
 
     @property
     def batch(self):
-        return int(self.q.shape[0])
+        return int(self.context_lens.shape[0])
 
     @property
     def max_blocks(self):
