@@ -124,12 +124,13 @@ def main():
     slots = torch.from_numpy(case.slot_mapping).to(dev)
     out = torch.empty_like(q)
     max_ctx = case.max_context
-    part = args.partition or default_partition(B, H, D, max_ctx)
+    part = args.partition            # 0: the library's default plan
+    strategy = "partitioned" if (part or default_partition(B, H, D, max_ctx)) else "flat"
     ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, part)), dtype=torch.uint8,
                      device=dev)
     kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
     log(f"workload: B={B} H={H} D={D} blocks={case.num_blocks} tokens={case.kv_tokens()} "
-        f"max_ctx={max_ctx} partition={part} kv_bytes={kv_bytes}")
+        f"max_ctx={max_ctx} strategy={strategy} partition={part} kv_bytes={kv_bytes}")
 
     def step(ev=None):
         kv_append(k_new, v_new, slots, kp, vp)
@@ -180,7 +181,8 @@ def main():
                         "kv_append of 1 token/sequence + pa_decode per step",
             "batch": B, "heads": H, "head_dim": D, "block_tokens": 16,
             "context_tokens": case.kv_tokens(), "max_context": max_ctx,
-            "num_blocks": case.num_blocks, "partition_tokens": part, "seed": 2,
+            "num_blocks": case.num_blocks, "strategy": strategy, "partition_tokens": part,
+            "seed": 2,
         },
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "seq_layers_per_s": round(B / (ms_per_step / 1e3), 1),
@@ -188,7 +190,7 @@ def main():
         "pa_decode_kv_gbs": round(dec_gbs, 2),
         "pa_decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
-            "kernel": "pa_decode (partition + merge kernels, one call)",
+            "kernel": "pa_decode (decode + merge kernels, one call)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

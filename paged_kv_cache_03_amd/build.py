@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedkv.so"
-SOURCES = ["api.hip", "pa_decode.hip", "cache_ops.hip"]
+SOURCES = ["api.hip", "pa_decode.hip", "pa_decode_flat.hip", "cache_ops.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -69,7 +69,7 @@ def build(verbose=False, save_temps=False):
         logs = list(ex.map(_run, cmds))
     lib = os.path.join(PKG_DIR, LIB_NAME)
     tmp = lib + ".tmp"
-    logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
+    logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]))
     os.replace(tmp, lib)
     if verbose:
         for log in logs:

@@ -40,20 +40,46 @@ bool partition_ok(int32_t part) {
                        part <= pkv::kMaxPartitionBlocks * kBlockTokens);
 }
 
-struct WsLayout {
-  int32_t max_parts = 0;
-  size_t ml_bytes = 0;
-  size_t total = 0;
+// How one decode call runs: the flat strategy by default (when its LDS
+// staging fits), the partitioned one for an explicit partition length or
+// very large batches.  A pure function of the shape.
+struct Plan {
+  bool flat = false;
+  int32_t part = 0;        // partitioned: tokens per partition
+  int32_t max_parts = 0;   // partitioned: partitions of the longest context
+  int32_t nr = 0;          // flat: ranges per head group
+  int32_t max_chunk = 0;   // flat: blocks in the longest range
+  size_t ml_bytes = 0;     // workspace: (m, l) area, 256-byte aligned
+  size_t total = 0;        // workspace bytes
 };
 
-WsLayout ws_layout(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t part) {
-  WsLayout w;
-  w.max_parts = max_ctx > 0 ? ceil_div(max_ctx, part) : 0;
-  if (w.max_parts <= 1) return w;
-  const size_t rows = (size_t)B * H * w.max_parts;
-  w.ml_bytes = round_up(rows * 2 * sizeof(float), kWsAlign);
-  w.total = w.ml_bytes + rows * D * sizeof(float);
-  return w;
+Plan make_plan(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t partition_tokens) {
+  Plan p;
+  const int32_t groups = H / waves_per_group(H);
+  const long long max_blocks = ceil_div(max_ctx, kBlockTokens);
+  if (partition_tokens == 0 && B > 0) {
+    const int32_t nr = pkv::kFlatGridTarget / groups > 0 ? pkv::kFlatGridTarget / groups : 1;
+    const long long t_max = (long long)B * max_blocks;
+    const long long chunk = (t_max + nr - 1) / nr;
+    if (pkv::flat_lds_bytes(B, (int)(chunk < (1 << 24) ? chunk : (1 << 24))) <=
+        (size_t)pkv::kFlatMaxLdsBytes) {
+      p.flat = true;
+      p.nr = nr;
+      p.max_chunk = (int32_t)chunk;
+      const size_t pieces = (size_t)H * nr * 2;
+      p.ml_bytes = round_up(pieces * 2 * sizeof(float), kWsAlign);
+      p.total = p.ml_bytes + pieces * D * sizeof(float);
+      return p;
+    }
+  }
+  p.part = partition_tokens ? partition_tokens : choose_partition(B, H, max_ctx);
+  p.max_parts = max_ctx > 0 ? ceil_div(max_ctx, p.part) : 0;
+  if (p.max_parts > 1) {
+    const size_t rows = (size_t)B * H * p.max_parts;
+    p.ml_bytes = round_up(rows * 2 * sizeof(float), kWsAlign);
+    p.total = p.ml_bytes + rows * D * sizeof(float);
+  }
+  return p;
 }
 
 bool decode_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx) {
@@ -82,14 +108,14 @@ const char* pkv_status_string(int code) {
 
 int32_t pkv_pa_decode_default_partition(int32_t B, int32_t H, int32_t D, int32_t max_context_len) {
   if (!decode_shape_ok(B, H, D, max_context_len)) return 0;
-  return choose_partition(B, H, max_context_len);
+  const Plan p = make_plan(B, H, D, max_context_len, 0);
+  return p.flat ? 0 : p.part;
 }
 
 size_t pkv_pa_decode_workspace_size_ex(int32_t B, int32_t H, int32_t D, int32_t max_context_len,
                                        int32_t partition_tokens) {
   if (!decode_shape_ok(B, H, D, max_context_len) || !partition_ok(partition_tokens)) return 0;
-  const int32_t part = partition_tokens ? partition_tokens : choose_partition(B, H, max_context_len);
-  return ws_layout(B, H, D, max_context_len, part).total;
+  return make_plan(B, H, D, max_context_len, partition_tokens).total;
 }
 
 size_t pkv_pa_decode_workspace_size(int32_t B, int32_t H, int32_t D, int32_t max_context_len) {
@@ -114,38 +140,62 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PKV_ERR_MISALIGNED;
 
-  const int32_t part = partition_tokens ? partition_tokens : choose_partition(B, H, max_context_len);
-  const WsLayout ws = ws_layout(B, H, D, max_context_len, part);
-  if (ws.total > 0) {
+  const Plan plan = make_plan(B, H, D, max_context_len, partition_tokens);
+  if (plan.total > 0) {
     if (!workspace) return PKV_ERR_NULL_PTR;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_MISALIGNED;
-    if (workspace_bytes < ws.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < plan.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
   }
   const int wpg = waves_per_group(H);
-  const long long grid = (long long)B * (H / wpg) * (ws.max_parts > 0 ? ws.max_parts : 1);
-  if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
-
-  pkv::PartArgs a;
-  a.q = static_cast<const _Float16*>(q);
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.out = static_cast<_Float16*>(out);
-  a.ws_ml = ws.total ? static_cast<float*>(workspace) : nullptr;
-  a.ws_acc = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_bytes) : nullptr;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.B = B;
-  a.H = H;
-  a.max_blocks = max_blocks_per_seq;
-  a.ctx_limit = max_context_len;
-  a.num_blocks = num_blocks;
-  a.part_blocks = part / kBlockTokens;
-  a.max_parts = ws.max_parts;
-  a.head_groups = H / wpg;
-  a.waves_per_group = wpg;
-  const hipError_t e = pkv::launch_pa_decode(a, D, (int)grid, wpg * 64,
-                                             static_cast<hipStream_t>(stream));
+  float* ws_ml = plan.total ? static_cast<float*>(workspace) : nullptr;
+  float* ws_acc =
+      plan.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes) : nullptr;
+  hipError_t e;
+  if (plan.flat) {
+    pkv::FlatArgs a;
+    a.q = static_cast<const _Float16*>(q);
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = static_cast<_Float16*>(out);
+    a.ws_ml = ws_ml;
+    a.ws_acc = ws_acc;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.B = B;
+    a.H = H;
+    a.max_blocks = max_blocks_per_seq;
+    a.ctx_limit = max_context_len;
+    a.num_blocks = num_blocks;
+    a.head_groups = H / wpg;
+    a.waves_per_group = wpg;
+    a.nr = plan.nr;
+    a.max_chunk = plan.max_chunk;
+    e = pkv::launch_pa_decode_flat(a, D, wpg * 64, static_cast<hipStream_t>(stream));
+  } else {
+    const long long grid = (long long)B * (H / wpg) * (plan.max_parts > 0 ? plan.max_parts : 1);
+    if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
+    pkv::PartArgs a;
+    a.q = static_cast<const _Float16*>(q);
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = static_cast<_Float16*>(out);
+    a.ws_ml = ws_ml;
+    a.ws_acc = ws_acc;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.B = B;
+    a.H = H;
+    a.max_blocks = max_blocks_per_seq;
+    a.ctx_limit = max_context_len;
+    a.num_blocks = num_blocks;
+    a.part_blocks = plan.part / kBlockTokens;
+    a.max_parts = plan.max_parts;
+    a.head_groups = H / wpg;
+    a.waves_per_group = wpg;
+    e = pkv::launch_pa_decode(a, D, (int)grid, wpg * 64, static_cast<hipStream_t>(stream));
+  }
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -41,6 +41,40 @@ struct MergeArgs {
   int max_parts;
 };
 
+// Flat strategy: every workgroup takes one of `nr` equal ranges of the
+// lined-up blocks of all sequences (see pa_decode_flat.hip).
+#ifndef PKV_FLAT_GRID
+#define PKV_FLAT_GRID 512
+#endif
+#ifndef PKV_FLAT_TILES
+#define PKV_FLAT_TILES 3
+#endif
+// Workgroups of 4 waves resident at once (256 CUs x 2 at the flat kernel's
+// register use) and tiles in each wave's load ring.
+constexpr int kFlatGridTarget = PKV_FLAT_GRID;
+constexpr int kFlatTiles = PKV_FLAT_TILES;
+constexpr int kFlatMaxLdsBytes = 32 * 1024;  // per workgroup, so LDS never limits residency
+
+struct FlatArgs {
+  const _Float16* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  _Float16* out;
+  float* ws_ml;        // [H][nr][2 pieces][2]: running max (log2 units), running sum
+  float* ws_acc;       // [H][nr][2 pieces][D]: unnormalised weighted sums
+  float scale_log2;
+  int B, H;
+  int max_blocks;
+  int ctx_limit;
+  int num_blocks;
+  int head_groups;
+  int waves_per_group;
+  int nr;              // ranges (workgroups) per head group
+  int max_chunk;       // longest range, in blocks (LDS sizing)
+};
+
 struct AppendArgs {
   const void* k;
   const void* v;
@@ -65,6 +99,8 @@ struct CowArgs {
 
 hipError_t launch_pa_decode(const PartArgs& part, int D, int grid_part, int threads,
                             hipStream_t stream);
+hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream);
+size_t flat_lds_bytes(int B, int max_chunk);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_cow_copy(const CowArgs& a, hipStream_t stream);
 

@@ -1,0 +1,338 @@
+// PagedAttention decode for gfx950 (MI355X): the flat strategy (default).
+//
+// Same result as the partitioned strategy ("PagedAttention", e-fortepiano.pl,
+// "Formulació matemàtica": attention computed block by block), organised for
+// a steady stream of loads:
+//
+//  * For one head, line up every block of every sequence, sequence after
+//    sequence: positions 0 .. T-1, with sequence b owning [S_b, S_{b+1}).
+//  * The grid is sized to what the GPU holds at once.  Workgroup i serves
+//    head group i % G (so, with G == 8, one XCD per head group and shared
+//    blocks found in that XCD's L2) and takes the i / G-th of NR equal,
+//    contiguous ranges of positions.  Every wave of the workgroup (one per
+//    head) streams through the whole range: no wave starts over at a
+//    partition boundary, and the ranges differ in length by at most one
+//    block.
+//  * A wave keeps a ring of kFlatTiles tiles in registers: while it works
+//    on one block the next ones are in flight.  The prefetch runs straight
+//    across sequence boundaries.
+//  * At each sequence boundary inside the range the running (m, l, acc) is
+//    closed: a sequence wholly inside the range is written as the final
+//    output; a sequence cut by the range's start or end leaves a partial
+//    result, at most two per wave ("head piece" = the range's first
+//    sequence begun earlier, "tail piece" = its last sequence going on
+//    later).  A second kernel merges the pieces of each cut sequence in
+//    ascending position order and writes zero rows for empty sequences.
+//
+// Block ids of the workgroup's range are staged once in LDS (one gather for
+// all its waves); the per-sequence block offsets come from a prefix sum of
+// the context lengths, computed in LDS by every workgroup.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "pa_common.h"
+
+namespace pkv {
+namespace {
+
+using namespace dev;
+
+__device__ __forceinline__ int clamp_ctx(int ctx, int limit) { return min(max(ctx, 0), limit); }
+
+// s_start[b] = blocks of the sequences before b (b <= B; s_start[B] = T);
+// s_tail[b] (if given) = tokens used in sequence b's last block.  All
+// threads of the workgroup take part; ends with a barrier.
+__device__ void block_prefix(const int32_t* ctx_lens, int B, int ctx_limit, int* s_start,
+                             int* s_tail, int* s_wave) {
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int per = (B + nt - 1) / nt;
+  const int lo = min(B, tid * per);
+  const int hi = min(B, lo + per);
+  int own = 0;
+  for (int b = lo; b < hi; ++b)
+    own += (clamp_ctx(ctx_lens[b], ctx_limit) + kBlockTokens - 1) / kBlockTokens;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  int incl = own;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int run = incl - own;
+  for (int w = 0; w < wave; ++w) run += s_wave[w];
+  for (int b = lo; b < hi; ++b) {
+    const int ctx = clamp_ctx(ctx_lens[b], ctx_limit);
+    const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
+    s_start[b] = run;
+    if (s_tail) s_tail[b] = ctx - (nb - 1) * kBlockTokens;
+    run += nb;
+  }
+  if (tid == nt - 1) s_start[B] = run;
+  __syncthreads();
+}
+
+// The sequence holding position s (0 <= s < T): the largest b with
+// s_start[b] <= s, which skips empty sequences.
+__device__ __forceinline__ int seq_of(const int* s_start, int B, int s) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_start[mid] <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One dword of the query row (b, h) per lane; lanes past the row read 0.
+template <int D>
+__device__ __forceinline__ uint32_t load_q_dword(const _Float16* q, size_t row,
+                                                 uint32_t lane_off4) {
+  return __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(q + row * D, D * 2), lane_off4, 0, 0);
+}
+
+// Spread a query row held one dword per lane into this lane's groups
+// 4*i + row (16 bytes each), through the wave's own 256-byte LDS slot: the
+// wave's LDS operations run in order, so no barrier is needed.
+template <int D>
+__device__ __forceinline__ void distribute_q(u4v (&q)[Geometry<D>::kLoads], uint32_t qn, int row,
+                                             int lane, uint32_t* slot) {
+  if (lane < D / 2) slot[lane] = qn;
+  const u4v* rows = reinterpret_cast<const u4v*>(slot);
+#pragma unroll
+  for (int i = 0; i < Geometry<D>::kLoads; ++i) q[i] = rows[4 * i + row];
+}
+
+// This lane's kOut output values (consecutive dims) as fp16 / fp32.
+template <int kOut>
+__device__ __forceinline__ void store_out(rsrc_t r, uint32_t off, const float (&val)[kOut],
+                                          float inv) {
+  if constexpr (kOut == 2) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 v = {(_Float16)(val[0] * inv), (_Float16)(val[1] * inv)};
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+  } else {
+    const _Float16 v = (_Float16)(val[0] * inv);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 0);
+  }
+}
+template <int kOut>
+__device__ __forceinline__ void store_acc(rsrc_t r, uint32_t off, const float (&val)[kOut]) {
+  if constexpr (kOut == 2) {
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    const u2v v = {as_u32(val[0]), as_u32(val[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(as_u32(val[0]), r, off, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void pa_decode_flat_kernel(FlatArgs a) {
+  constexpr int kAcc = Geometry<D>::kAcc;
+  constexpr int kTile = Geometry<D>::kTileBytes;
+  constexpr int kOut = Geometry<D>::kOutPerLane;
+  extern __shared__ int smem[];
+  __shared__ int s_wave[4];
+  __shared__ uint32_t s_q[4][kWave];   // per-wave query staging
+  int* s_start = smem;                 // B + 1
+  int* s_tail = smem + a.B + 1;        // B
+  int* s_ids = smem + 2 * a.B + 1;     // up to max_chunk
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int token = lane % kBlockTokens;
+  const int row = lane / kBlockTokens;
+  const int g = blockIdx.x % a.head_groups;
+  const int r = blockIdx.x / a.head_groups;
+  const int h = g * a.waves_per_group + wave;
+
+  block_prefix(a.context_lens, a.B, a.ctx_limit, s_start, s_tail, s_wave);
+  const int T = s_start[a.B];
+  const int chunk = (T + a.nr - 1) / a.nr;
+  const int c0 = min(T, r * chunk);
+  const int c1 = min(T, c0 + chunk);
+  if (c0 >= c1) return;                // uniform for the workgroup
+
+  for (int s = c0 + tid; s < c1; s += blockDim.x) {
+    const int b = seq_of(s_start, a.B, s);
+    const int id = a.block_tables[(size_t)b * a.max_blocks + (s - s_start[b])];
+    s_ids[s - c0] = min(max(id, 0), a.num_blocks - 1);
+  }
+  __syncthreads();
+
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
+  const size_t block_stride = (size_t)a.H * kTile;
+  const uint32_t lane_off = lane * 16u;
+  auto fetch = [&](Tile<D>& t, int s) {
+    const int j = min(s, c1 - 1) - c0;
+    const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[j]) * block_stride;
+    load_tile<D>(t, make_rsrc(kbase + o, kTile), make_rsrc(vbase + o, kTile), lane_off);
+  };
+
+  // Current segment: sequence b, positions [seg_lo, seg_hi) of its
+  // [seq_lo, seq_hi).  All wave-uniform.
+  int b = seq_of(s_start, a.B, c0);
+  int seq_lo = s_start[b];
+  int seq_hi = s_start[b + 1];
+  int seg_lo = c0;
+  int seg_hi = min(c1, seq_hi);
+  int tail = s_tail[b];
+
+  const uint32_t lane_off4 = lane * 4u;
+  u4v q[Geometry<D>::kLoads];
+  distribute_q<D>(q, load_q_dword<D>(a.q, (size_t)b * a.H + h, lane_off4), row, lane,
+                  s_q[wave]);
+  int b_next = b;
+  uint32_t qn = 0;
+  if (seg_hi < c1) {                   // the next segment's query, one segment ahead
+    b_next = seq_of(s_start, a.B, seg_hi);
+    qn = load_q_dword<D>(a.q, (size_t)b_next * a.H + h, lane_off4);
+  }
+  // Per-lane byte offsets of this lane's output values (fixed for the wave;
+  // see reduce_rows), and of the (m, l) pair written by lane 0.
+  const int d0 = (4 * ((token * kOut) / 8) + row) * 8 + (token * kOut) % 8;
+  const uint32_t out_off = d0 * 2u;
+  const uint32_t acc_off = d0 * 4u;
+
+
+  float m = kNegInf, l = 0.0f;
+  float acc[kAcc];
+#pragma unroll
+  for (int j = 0; j < kAcc; ++j) acc[j] = 0.0f;
+
+  auto step = [&](const Tile<D>& t, int s) {
+    // one code path for every block: only a sequence's last block can be
+    // partially filled, the others pass valid = 16
+    consume<D, true>(t, q, a.scale_log2, token, s == seq_hi - 1 ? tail : kBlockTokens, m, l, acc);
+    if (s != seg_hi - 1) return;
+    // close the segment
+    float val[kOut];
+    reduce_rows<D>(l, acc, token, row, val);
+    if (seg_lo == seq_lo && seg_hi == seq_hi) {
+      const rsrc_t orow = make_rsrc(a.out + ((size_t)b * a.H + h) * D, D * 2);
+      const float inv = 1.0f / l;
+      store_out<kOut>(orow, out_off, val, inv);
+    } else {
+      const size_t piece = ((size_t)h * a.nr + r) * 2 + (seg_lo > seq_lo ? 0 : 1);
+      store_acc<kOut>(make_rsrc(a.ws_acc + piece * D, D * 4), acc_off, val);
+      // (m, l) as one 8-byte store; only lane 0 is inside the 8-byte resource
+      typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+      const u2v ml = {as_u32(m), as_u32(l)};
+      __builtin_amdgcn_raw_buffer_store_b64(ml, make_rsrc(a.ws_ml + piece * 2, 8), lane * 8u, 0, 0);
+    }
+    if (seg_hi < c1) {                 // open the next one
+      b = b_next;
+      seq_lo = s_start[b];
+      seq_hi = s_start[b + 1];
+      seg_lo = seg_hi;
+      seg_hi = min(c1, seq_hi);
+      tail = s_tail[b];
+      distribute_q<D>(q, qn, row, lane, s_q[wave]);
+      if (seg_hi < c1) {
+        b_next = seq_of(s_start, a.B, seg_hi);
+        qn = load_q_dword<D>(a.q, (size_t)b_next * a.H + h, lane_off4);
+      }
+      m = kNegInf;
+      l = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[j] = 0.0f;
+    }
+  };
+
+  // kFlatTiles tiles in rotation: while one is consumed the next
+  // kFlatTiles - 1 are in flight.  The prefetch index is clamped to the
+  // range's last block (re-reading it is an L1/L2 hit), so every iteration
+  // issues the same loads and the load counters stay exact.
+  Tile<D> t[kFlatTiles];
+#pragma unroll
+  for (int k = 0; k + 1 < kFlatTiles; ++k) fetch(t[k], c0 + k);
+  // Exits jump out of the unrolled body, so no skipped step ever flows
+  // back into the loop head (that would make the compiler drain every load).
+  int s = c0;
+  for (;;) {
+#pragma unroll
+    for (int k = 0; k < kFlatTiles; ++k) {
+      fetch(t[(k + kFlatTiles - 1) % kFlatTiles], s + kFlatTiles - 1);
+      step(t[k], s);
+      if (++s >= c1) goto done;
+    }
+  }
+done:;
+}
+
+// One workgroup per sequence: zero rows for an empty sequence; for a
+// sequence cut across ranges, merge its pieces (weights exp2(m_r - M)) in
+// ascending range order.
+template <int D>
+__global__ __launch_bounds__(256) void pa_decode_flat_merge_kernel(FlatArgs a) {
+  extern __shared__ int smem[];
+  __shared__ int s_wave[4];
+  int* s_start = smem;
+  block_prefix(a.context_lens, a.B, a.ctx_limit, s_start, nullptr, s_wave);
+  const int T = s_start[a.B];
+  const int chunk = (T + a.nr - 1) / a.nr;
+  const int b = blockIdx.x;
+  const int S = s_start[b];
+  const int E = s_start[b + 1];
+  const size_t out_row = (size_t)b * a.H * D;
+  if (E == S) {
+    for (int i = threadIdx.x; i < a.H * D; i += blockDim.x) a.out[out_row + i] = (_Float16)0.0f;
+    return;
+  }
+  const int r0 = S / chunk;
+  const int r1 = (E - 1) / chunk;
+  if (r0 == r1) return;                // written whole by the decode kernel
+  for (int i = threadIdx.x; i < a.H * (D / 2); i += blockDim.x) {
+    const int h = i / (D / 2);
+    const int d = (i % (D / 2)) * 2;
+    float mx = kNegInf;
+    for (int rr = r0; rr <= r1; ++rr) {
+      const size_t piece = ((size_t)h * a.nr + rr) * 2 + (rr * chunk > S ? 0 : 1);
+      mx = fmaxf(mx, a.ws_ml[piece * 2]);
+    }
+    float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+    for (int rr = r0; rr <= r1; ++rr) {
+      const size_t piece = ((size_t)h * a.nr + rr) * 2 + (rr * chunk > S ? 0 : 1);
+      const float w = exp2f(a.ws_ml[piece * 2] - mx);
+      den = fmaf(w, a.ws_ml[piece * 2 + 1], den);
+      n0 = fmaf(w, a.ws_acc[piece * D + d], n0);
+      n1 = fmaf(w, a.ws_acc[piece * D + d + 1], n1);
+    }
+    const float inv = 1.0f / den;
+    a.out[out_row + (size_t)h * D + d] = (_Float16)(n0 * inv);
+    a.out[out_row + (size_t)h * D + d + 1] = (_Float16)(n1 * inv);
+  }
+}
+
+}  // namespace
+
+size_t flat_lds_bytes(int B, int max_chunk) {
+  return (size_t)(2 * B + 1 + max_chunk) * sizeof(int);
+}
+
+hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream) {
+  const size_t lds = flat_lds_bytes(a.B, a.max_chunk);
+  const int grid = a.head_groups * a.nr;
+  if (D == 128)
+    hipLaunchKernelGGL(pa_decode_flat_kernel<128>, dim3(grid), dim3(threads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(pa_decode_flat_kernel<64>, dim3(grid), dim3(threads), lds, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds_merge = (size_t)(a.B + 1) * sizeof(int);
+  if (D == 128)
+    hipLaunchKernelGGL(pa_decode_flat_merge_kernel<128>, dim3(a.B), dim3(256), lds_merge, stream, a);
+  else
+    hipLaunchKernelGGL(pa_decode_flat_merge_kernel<64>, dim3(a.B), dim3(256), lds_merge, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

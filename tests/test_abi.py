@@ -94,19 +94,29 @@ def test_plain_decode_entry_checks_too(lib):
 
 def test_workspace_size(lib):
     B, H, D, ctx = 200, 32, 128, 2048
-    part = lib.pkv_pa_decode_default_partition(B, H, D, ctx)
-    assert part % 16 == 0 and 16 <= part <= 512
+    # default plan: the flat strategy, whose partial pieces do not grow with
+    # the context (at most two per workgroup range and head)
+    assert lib.pkv_pa_decode_default_partition(B, H, D, ctx) == 0
+    flat = lib.pkv_pa_decode_workspace_size(B, H, D, ctx)
+    assert 0 < flat < (16 << 20)
+    assert lib.pkv_pa_decode_workspace_size(B, H, D, 1024) == flat
+    assert lib.pkv_pa_decode_workspace_size(10, H, D, ctx) == flat
+    # explicit partitions: one (m, l, acc[D]) slot per (sequence, head, partition)
+    part = 256
     np_ = -(-ctx // part)
     rows = B * H * np_
     ml = -(-rows * 8 // 256) * 256
-    assert lib.pkv_pa_decode_workspace_size(B, H, D, ctx) == ml + rows * D * 4
+    assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, ctx, part) == ml + rows * D * 4
     # a context that fits one partition needs no workspace
     assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, 256, 256) == 0
     assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, 257, 256) > 0
     assert lib.pkv_pa_decode_workspace_size_ex(B, H, D, 100, 24) == 0     # invalid partition
     assert lib.pkv_pa_decode_workspace_size(B, H, 96, 100) == 0           # invalid D
-    # small batches are split finer to fill the GPU
-    assert lib.pkv_pa_decode_default_partition(1, 32, 128, 2048) < part
+    # very large batches fall back to partitions, split finer when short
+    big = lib.pkv_pa_decode_default_partition(8192, H, D, ctx)
+    assert big % 16 == 0 and 16 <= big <= 512
+    assert lib.pkv_pa_decode_workspace_size(8192, H, D, ctx) == \
+        lib.pkv_pa_decode_workspace_size_ex(8192, H, D, ctx, big)
 
 
 def append(lib, **kw):
