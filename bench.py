@@ -2,7 +2,7 @@
 
 One step = one pass of the hot path over one batch: append one new token per
 sequence into its slot (kv_append), then decode every sequence over its
-whole context (pa_decode: partition kernel + merge kernel).  The workload is
+whole context (pa_decode: decode kernel + merge kernel).  The workload is
 one layer of a GPT-style model, batch 200, 32 heads x 128 dims, fp16,
 16-token blocks, contexts = prompt U[32,256] + response geometric(mean 500)
 capped at 2048, pool = blocks needed + 10% free, tables from a shuffled free
@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-KV_BYTES_PER_TOKEN_LAYER = None  # set from the shape: 2 * H * D * 2
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_flat_batch200_hbm_traffic.json")
 
 
 def log(msg):
@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = default)")
+    ap.add_argument("--workload", default="batch200",
+                    choices=["batch200", "batch10", "shared_prefix", "full_step", "beam_step"],
+                    help="batch200 (default): the headline one-layer batch of 200")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0,
                     help="sequences in the oracle sample (0 = sized to ~15 s)")
@@ -52,6 +55,35 @@ def algorithmic_bytes(lens, H, D):
     qo = len(lens) * H * D * 2 * 2
     tab = sum(4 * math.ceil(n / 16) + 4 for n in lens)
     return kv, kv + qo + tab
+
+
+def kernel_source_sha256():
+    """Hash of the kernel sources and the C header, to tell whether stored
+    counter figures still describe the code that runs."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    rels = sorted(glob.glob(os.path.join("paged_kv_cache_03_amd", "csrc", "*.hip"), root_dir=ROOT) +
+                  glob.glob(os.path.join("paged_kv_cache_03_amd", "csrc", "*.h"), root_dir=ROOT))
+    for rel in rels + [os.path.join("include", "pagedkv.h")]:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per pa_decode call from the committed rocprofv3 counter
+    passes (FETCH_SIZE, WRITE_SIZE, calibrated against a 1 GiB copy), or None
+    once the kernel sources differ from the ones they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return int(rec["pa_decode_hbm_bytes_per_call"])
 
 
 def cpu_baseline(case, kp, vp, torch, budget_s=15.0, nseq=0):
@@ -91,6 +123,146 @@ def cpu_baseline(case, kp, vp, torch, budget_s=15.0, nseq=0):
     }
 
 
+class Run:
+    """One benchmark workload: what a step does and how to count it."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def setup_batch(torch, dev, wl, args, batch, seed):
+    """One layer; each step appends one token per sequence and decodes."""
+    from paged_kv_cache_03_amd import default_partition, kv_append, pa_decode, pa_decode_workspace_size
+    case = wl.gpt_batch(batch, seed=seed, append=True, fill=False)
+    B, H, D = case.batch, case.num_heads, case.head_dim
+    kp = wl.device_pool(torch, case, 0, 0, dev)
+    vp = wl.device_pool(torch, case, 0, 1, dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    q, tables, lens = t(case.q), t(case.block_tables), t(case.context_lens)
+    k_new, v_new, slots = t(case.k_new), t(case.v_new), t(case.slot_mapping)
+    out = torch.empty_like(q)
+    max_ctx = case.max_context
+    part = args.partition
+    strategy = "partitioned" if (part or default_partition(B, H, D, max_ctx)) else "flat"
+    ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, part)), dtype=torch.uint8,
+                     device=dev)
+    kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
+
+    def step(events):
+        kv_append(k_new, v_new, slots, kp, vp)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+        pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
+                  workspace=ws, partition_tokens=part)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+
+    return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
+               algo_bytes=algo_bytes, strategy=strategy, part=part, extra={},
+               config={"workload": f"one layer, batch {B}, 32 heads x 128 dims fp16, 16-token "
+                                   "blocks, contexts prompt U[32,256] + geometric(mean 500) "
+                                   "capped at 2048, kv_append of 1 token/sequence + pa_decode "
+                                   "per step",
+                       "batch": B, "heads": H, "head_dim": D, "block_tokens": 16,
+                       "context_tokens": case.kv_tokens(), "max_context": max_ctx,
+                       "num_blocks": case.num_blocks, "strategy": strategy,
+                       "partition_tokens": part, "seed": seed})
+
+
+def setup_shared_prefix(torch, dev, wl, args):
+    """One layer, 100 sequences sharing a 1024-token prefix; each step copies
+    the prefix's last block per sequence (copy-on-write) and decodes."""
+    from paged_kv_cache_03_amd import cow_copy_blocks, pa_decode, pa_decode_workspace_size
+    case = wl.shared_prefix(fill=False)
+    B, H, D = case.batch, case.num_heads, case.head_dim
+    kp = wl.device_pool(torch, case, 0, 0, dev)
+    vp = wl.device_pool(torch, case, 0, 1, dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    q, tables, lens, pairs = t(case.q), t(case.block_tables), t(case.context_lens), t(case.cow_pairs)
+    out = torch.empty_like(q)
+    max_ctx = case.max_context
+    ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, args.partition)),
+                     dtype=torch.uint8, device=dev)
+    kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
+    import numpy as np
+    used = np.unique(case.block_tables[case.block_tables >= 0])
+    unique_bytes = int(used.size) * H * 16 * D * 2 * 2
+
+    def step(events):
+        cow_copy_blocks(pairs, [kp], [vp])
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+        pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
+                  workspace=ws, partition_tokens=args.partition, keep_cached=True)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+
+    return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
+               algo_bytes=algo_bytes, strategy="flat" if not args.partition else "partitioned",
+               part=args.partition, extra={"unique_kv_bytes": unique_bytes, "keep_cached": True},
+               config={"workload": "one layer, batch 100, a 1024-token prefix in 64 shared "
+                                   "blocks + private suffix U[0,500]; per step copy-on-write of "
+                                   "the prefix's last block for each sequence + pa_decode",
+                       "batch": B, "heads": H, "head_dim": D, "block_tokens": 16,
+                       "context_tokens": case.kv_tokens(), "max_context": max_ctx,
+                       "num_blocks": case.num_blocks, "seed": 3})
+
+
+def setup_full_step(torch, dev, wl, args, beams):
+    """32 layers x 200 sequences x 2048 tokens; per step (beam groups:
+    copy-on-write of each beam's last block in every layer, then) per layer
+    append one token per sequence and decode."""
+    from paged_kv_cache_03_amd import cow_copy_blocks, kv_append, pa_decode, pa_decode_workspace_size
+    case = wl.full_step(beams=beams)
+    B, H, D, L = case.batch, case.num_heads, case.head_dim, case.num_layers
+    per_pool = case.num_blocks * H * 16 * D * 2
+    free, _ = torch.cuda.mem_get_info(dev)
+    distinct = max(1, min(L, int((free - (8 << 30)) // (2 * per_pool))))
+    log(f"{L} layers, {distinct} distinct layer pools of {2 * per_pool / 2**30:.2f} GiB")
+    pools = [(wl.device_pool(torch, case, l, 0, dev), wl.device_pool(torch, case, l, 1, dev))
+             for l in range(distinct)]
+    t = lambda a: torch.from_numpy(a).to(dev)
+    qs = [t(case.q[l]) for l in range(L)]
+    kn = [t(case.k_new[l]) for l in range(L)]
+    vn = [t(case.v_new[l]) for l in range(L)]
+    tables, lens, slots = t(case.block_tables), t(case.context_lens), t(case.slot_mapping)
+    pairs = t(case.cow_pairs) if case.cow_pairs is not None else None
+    out = torch.empty_like(qs[0])
+    ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, 2048, args.partition)),
+                     dtype=torch.uint8, device=dev)
+    kv_layer, algo_layer = algorithmic_bytes(case.context_lens, H, D)
+    layer_pools = [pools[l % distinct] for l in range(L)]
+
+    def step(events):
+        if pairs is not None:
+            cow_copy_blocks(pairs, [p[0] for p in pools], [p[1] for p in pools])
+        for l in range(L):
+            kp, vp = layer_pools[l]
+            kv_append(kn[l], vn[l], slots, kp, vp)
+            events.append(torch.cuda.Event(enable_timing=True))
+            events[-1].record()
+            pa_decode(qs[l], kp, vp, tables, lens, case.scale, out, max_context_len=2048,
+                      workspace=ws, partition_tokens=args.partition, keep_cached=beams > 1)
+            events.append(torch.cuda.Event(enable_timing=True))
+            events[-1].record()
+
+    import numpy as np
+    used = np.unique(case.block_tables)
+    return Run(case=case, kp=pools[0][0], vp=pools[0][1], step=step, seqs_per_step=B * L,
+               kv_bytes=kv_layer * L, algo_bytes=algo_layer,
+               strategy="flat" if not args.partition else "partitioned", part=args.partition,
+               extra={"layers": L, "distinct_layer_pools": distinct, "keep_cached": beams > 1,
+                      "unique_kv_bytes_per_layer": int(used.size) * H * 16 * D * 2 * 2},
+               config={"workload": f"full decode step: {L} layers x batch {B} x 2048 tokens, "
+                                   "32 heads x 128 dims fp16; per layer kv_append + pa_decode"
+                                   + (f"; {beams}-beam groups sharing all but the last block, "
+                                      "copy-on-write of the last block per beam" if beams > 1
+                                      else ""),
+                       "batch": B, "layers": L, "heads": H, "head_dim": D, "block_tokens": 16,
+                       "context_tokens_per_layer": case.kv_tokens(), "num_blocks": case.num_blocks,
+                       "beams": beams, "seed": 4})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -101,8 +273,7 @@ def main():
     import torch
 
     import workloads as wl
-    from paged_kv_cache_03_amd import (kv_append, load_library, pa_decode,
-                                       pa_decode_workspace_size, default_partition)
+    from paged_kv_cache_03_amd import load_library
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -112,56 +283,38 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")
 
-    case = wl.gpt_batch(200, seed=2, append=True, fill=False)
-    B, H, D = case.batch, case.num_heads, case.head_dim
-    kp = wl.device_pool(torch, case, 0, 0, dev)
-    vp = wl.device_pool(torch, case, 0, 1, dev)
-    q = torch.from_numpy(case.q).to(dev)
-    tables = torch.from_numpy(case.block_tables).to(dev)
-    lens = torch.from_numpy(case.context_lens).to(dev)
-    k_new = torch.from_numpy(case.k_new).to(dev)
-    v_new = torch.from_numpy(case.v_new).to(dev)
-    slots = torch.from_numpy(case.slot_mapping).to(dev)
-    out = torch.empty_like(q)
-    max_ctx = case.max_context
-    part = args.partition            # 0: the library's default plan
-    strategy = "partitioned" if (part or default_partition(B, H, D, max_ctx)) else "flat"
-    ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, part)), dtype=torch.uint8,
-                     device=dev)
-    kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
-    log(f"workload: B={B} H={H} D={D} blocks={case.num_blocks} tokens={case.kv_tokens()} "
-        f"max_ctx={max_ctx} strategy={strategy} partition={part} kv_bytes={kv_bytes}")
-
-    def step(ev=None):
-        kv_append(k_new, v_new, slots, kp, vp)
-        if ev is not None:
-            ev[0].record()
-        pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
-                  workspace=ws, partition_tokens=part)
-        if ev is not None:
-            ev[1].record()
+    if args.workload == "batch200":
+        run = setup_batch(torch, dev, wl, args, 200, 2)
+    elif args.workload == "batch10":
+        run = setup_batch(torch, dev, wl, args, 10, 1)
+    elif args.workload == "shared_prefix":
+        run = setup_shared_prefix(torch, dev, wl, args)
+    else:
+        run = setup_full_step(torch, dev, wl, args, 4 if args.workload == "beam_step" else 1)
+    log(f"workload {args.workload}: {run.config}")
 
     for _ in range(args.warmup):
-        step()
+        run.step([])
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        run.step(events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
-    dec_ms = [s.elapsed_time(e) for s, e in events]
+    dec_ms = [events[i].elapsed_time(events[i + 1]) for i in range(0, len(events), 2)]
     dec_avg_s = float(np.mean(dec_ms)) / 1e3
     ms_per_step = elapsed * 1e3 / args.steps
 
-    step_gbs = kv_bytes / (ms_per_step / 1e3) / 1e9
-    dec_gbs = kv_bytes / dec_avg_s / 1e9
-    achieved = algo_bytes / dec_avg_s / 1e9
+    step_gbs = run.kv_bytes / (ms_per_step / 1e3) / 1e9
+    kv_per_call = run.kv_bytes / (len(dec_ms) / args.steps)
+    dec_gbs = kv_per_call / dec_avg_s / 1e9
+    achieved = run.algo_bytes / dec_avg_s / 1e9
+    headline = args.workload == "batch200" and run.strategy == "flat"
     result = {
         "metric": "pa_decode K/V GB/s (% MI355X HBM peak) + seq-layers/s at batch 200",
         "value": round(step_gbs, 2),
@@ -175,17 +328,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {
-            "workload": "one layer, batch 200, 32 heads x 128 dims fp16, 16-token blocks, "
-                        "contexts prompt U[32,256] + geometric(mean 500) capped at 2048, "
-                        "kv_append of 1 token/sequence + pa_decode per step",
-            "batch": B, "heads": H, "head_dim": D, "block_tokens": 16,
-            "context_tokens": case.kv_tokens(), "max_context": max_ctx,
-            "num_blocks": case.num_blocks, "strategy": strategy, "partition_tokens": part,
-            "seed": 2,
-        },
+        "config": run.config,
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
-        "seq_layers_per_s": round(B / (ms_per_step / 1e3), 1),
+        "seq_layers_per_s": round(run.seqs_per_step / (ms_per_step / 1e3), 1),
         "pa_decode_us": round(dec_avg_s * 1e6, 3),
         "pa_decode_kv_gbs": round(dec_gbs, 2),
         "pa_decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
@@ -196,10 +341,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": algo_bytes,
-            "traffic": None,
+            "bytes_per_launch": run.algo_bytes,
+            "traffic": measured_traffic() if headline else None,
         },
     }
+    result.update(run.extra)
 
     if args.copy_probe:
         n = 1 << 30
@@ -218,9 +364,9 @@ def main():
                                 "gbs_read_plus_write": round(2 * n / t / 1e9, 1)}
         del src, dst
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "batch200":
         log("timing the oracle on a sample of the workload (cpu baseline)")
-        result["cpu_baseline"] = cpu_baseline(case, kp, vp, torch, nseq=args.cpu_seqs)
+        result["cpu_baseline"] = cpu_baseline(run.case, run.kp, run.vp, torch, nseq=args.cpu_seqs)
         log(f"cpu baseline: {result['cpu_baseline']['sample']}")
     print(json.dumps(result), flush=True)
 

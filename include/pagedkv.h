@@ -69,10 +69,12 @@ enum pkv_status {
 #define PKV_BLOCK_TOKENS 16
 
 /*
- * Bytes of device workspace pkv_pa_decode needs for this shape (0 when every
- * sequence fits in one partition).  Pure host function; max_context_len is
- * the largest entry of context_lens the caller will pass.  Returns 0 for
- * invalid sizes.
+ * Bytes of device workspace pkv_pa_decode needs for this shape.  Pure host
+ * function; max_context_len is the largest entry of context_lens the caller
+ * will pass.  Returns 0 for invalid sizes (and for the partitioned strategy
+ * when every sequence fits in one partition).  The workspace holds
+ * intermediate results only: its contents need no initialisation and are
+ * not meaningful after the call.
  */
 size_t pkv_pa_decode_workspace_size(int32_t B, int32_t H, int32_t D,
                                     int32_t max_context_len);
@@ -85,12 +87,17 @@ size_t pkv_pa_decode_workspace_size(int32_t B, int32_t H, int32_t D,
  *
  * over t = 0 .. context_lens[b]-1, where K_t / V_t are read from physical
  * block block_tables[b][t/16] at position t%16 of k_pool / v_pool.  The
- * result is computed block by block in fp32 with an online softmax and,
- * for long contexts, split into partitions whose partial results are merged
- * in ascending partition order; it is rounded to fp16 (round to nearest
- * even).  A sequence with context 0 gets a zero row.  The arithmetic order
- * depends only on logical positions, so moving blocks to other physical ids
- * or sharing them between sequences does not change any output bit.
+ * result is computed block by block in fp32 with an online softmax and
+ * rounded to fp16 (round to nearest even); a sequence with context 0 gets a
+ * zero row.  By default the blocks of all sequences are lined up and cut
+ * into equal ranges, one per resident workgroup; a sequence cut by a range
+ * boundary leaves partial results that are merged in ascending position
+ * order (with pkv_pa_decode_ex and a partition length, each sequence is cut
+ * into fixed partitions instead).  The arithmetic order depends only on the
+ * logical positions and the context lengths of the batch, so moving blocks
+ * to other physical ids or sharing them between sequences does not change
+ * any output bit.  K/V tiles are streamed with a non-temporal cache policy
+ * (see PKV_DECODE_KEEP_KV_CACHED).
  *
  * device: q, k_pool, v_pool, out (16-byte aligned), block_tables,
  *         context_lens, workspace (256-byte aligned, may be NULL when the
@@ -106,10 +113,21 @@ int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
                   int32_t num_blocks, float scale, void* out,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Flags of pkv_pa_decode_ex. */
+#define PKV_DECODE_KEEP_KV_CACHED 1u  /* load K/V tiles with the normal cache
+                                         policy instead of streaming them
+                                         (non-temporal): for batches whose
+                                         tables share physical blocks (a
+                                         shared prompt, forks), so that
+                                         repeated blocks are found in L2.
+                                         Results are identical either way. */
+
 /*
  * pkv_pa_decode with an explicit partition length in tokens (a positive
- * multiple of 16, at most 512), or 0 for the default choice.  The workspace
- * size for it is pkv_pa_decode_workspace_size_ex with the same value.
+ * multiple of 16, at most 512), or 0 for the default choice, and flags
+ * (0 or PKV_DECODE_KEEP_KV_CACHED; other bits are rejected with
+ * PKV_ERR_BAD_SHAPE).  The workspace size for it is
+ * pkv_pa_decode_workspace_size_ex with the same partition value.
  */
 int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -117,13 +135,15 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
                      int32_t B, int32_t H, int32_t D, int32_t block_size,
                      int32_t num_blocks, float scale, void* out,
                      void* workspace, size_t workspace_bytes,
-                     int32_t partition_tokens, void* stream);
+                     int32_t partition_tokens, uint32_t flags, void* stream);
 
 size_t pkv_pa_decode_workspace_size_ex(int32_t B, int32_t H, int32_t D,
                                        int32_t max_context_len,
                                        int32_t partition_tokens);
 
-/* Partition length in tokens that pkv_pa_decode picks for this shape. */
+/* Partition length in tokens that pkv_pa_decode uses for this shape, or 0
+ * when it uses the default range strategy (every batch whose sequence
+ * offsets and range block ids fit the workgroup's LDS budget). */
 int32_t pkv_pa_decode_default_partition(int32_t B, int32_t H, int32_t D,
                                         int32_t max_context_len);
 

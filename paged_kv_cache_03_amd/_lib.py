@@ -10,7 +10,8 @@ import threading
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libpagedkv.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
+DECODE_KEEP_KV_CACHED = 1
 
 # Status codes (enum pkv_status)
 OK = 0
@@ -33,7 +34,8 @@ SIGNATURES = {
     "pkv_pa_decode": (_c.c_int, [_vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _c.c_float, _vp, _vp, _c.c_size_t, _vp]),
     "pkv_pa_decode_ex": (_c.c_int, [_vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32,
-                                    _i32, _i32, _c.c_float, _vp, _vp, _c.c_size_t, _i32, _vp]),
+                                    _i32, _i32, _c.c_float, _vp, _vp, _c.c_size_t, _i32,
+                                    _c.c_uint32, _vp]),
     "pkv_kv_append": (_c.c_int, [_vp, _vp, _i32p, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pkv_cow_copy_blocks": (_c.c_int, [_c.POINTER(_vp), _c.POINTER(_vp), _i32, _i32p, _i32, _i32,
                                        _c.c_int64, _vp]),

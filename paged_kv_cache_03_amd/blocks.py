@@ -183,6 +183,19 @@ class PagedRequest:
         return self.num_pages * self.pool.page_tokens - self.num_tokens
 
 
+def tables_share_blocks(requests):
+    """Whether any physical page appears more than once across the batch's
+    block tables (a shared prompt, forked branches): then the decode should
+    keep K/V in the caches rather than stream it."""
+    seen = set()
+    for r in requests:
+        for page in r.block_table:
+            if page in seen:
+                return True
+            seen.add(page)
+    return False
+
+
 def device_arrays(requests, width=None):
     """Block tables ([B][width] int32, -1 padded) and context lengths ([B]
     int32) for a batch of requests."""

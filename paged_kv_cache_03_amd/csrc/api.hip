@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kBlockTokens = PKV_BLOCK_TOKENS;
 constexpr size_t kWsAlign = 256;
 // Enough workgroups to keep all 256 CUs busy several times over.
@@ -23,6 +23,13 @@ bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int waves_per_group(int32_t H) { return (H % 4 == 0) ? 4 : (H % 2 == 0) ? 2 : 1; }
+// Heads per workgroup of the flat strategy: the largest power of two up to
+// kFlatMaxWaves that divides H.
+int flat_waves_per_group(int32_t H) {
+  int w = pkv::kFlatMaxWaves;
+  while (w > 1 && H % w) w /= 2;
+  return w;
+}
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
@@ -50,14 +57,15 @@ struct Plan {
   int32_t nr = 0;          // flat: ranges per head group
   int32_t max_chunk = 0;   // flat: blocks in the longest range
   size_t ml_bytes = 0;     // workspace: (m, l) area, 256-byte aligned
+  size_t seq_offset = 0;   // flat: byte offset of the sequence offsets
   size_t total = 0;        // workspace bytes
 };
 
 Plan make_plan(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t partition_tokens) {
   Plan p;
-  const int32_t groups = H / waves_per_group(H);
   const long long max_blocks = ceil_div(max_ctx, kBlockTokens);
   if (partition_tokens == 0 && B > 0) {
+    const int32_t groups = H / flat_waves_per_group(H);
     const int32_t nr = pkv::kFlatGridTarget / groups > 0 ? pkv::kFlatGridTarget / groups : 1;
     const long long t_max = (long long)B * max_blocks;
     const long long chunk = (t_max + nr - 1) / nr;
@@ -68,7 +76,8 @@ Plan make_plan(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t partiti
       p.max_chunk = (int32_t)chunk;
       const size_t pieces = (size_t)H * nr * 2;
       p.ml_bytes = round_up(pieces * 2 * sizeof(float), kWsAlign);
-      p.total = p.ml_bytes + pieces * D * sizeof(float);
+      p.seq_offset = p.ml_bytes + round_up(pieces * D * sizeof(float), kWsAlign);
+      p.total = p.seq_offset + (size_t)(B + 1) * sizeof(int32_t);
       return p;
     }
   }
@@ -127,8 +136,10 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
                      int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
                      void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                     void* stream) {
+                     uint32_t flags, void* stream) {
   if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)PKV_DECODE_KEEP_KV_CACHED) return PKV_ERR_BAD_SHAPE;
+  const bool keep_cached = (flags & PKV_DECODE_KEEP_KV_CACHED) != 0;
   if (!decode_shape_ok(B, H, D, max_context_len) || !partition_ok(partition_tokens))
     return PKV_ERR_BAD_SHAPE;
   if (B == 0) return PKV_OK;
@@ -152,6 +163,7 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
       plan.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes) : nullptr;
   hipError_t e;
   if (plan.flat) {
+    const int fw = flat_waves_per_group(H);
     pkv::FlatArgs a;
     a.q = static_cast<const _Float16*>(q);
     a.k_pool = k_pool;
@@ -161,17 +173,19 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
     a.out = static_cast<_Float16*>(out);
     a.ws_ml = ws_ml;
     a.ws_acc = ws_acc;
+    a.ws_seq = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.seq_offset);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.B = B;
     a.H = H;
     a.max_blocks = max_blocks_per_seq;
     a.ctx_limit = max_context_len;
     a.num_blocks = num_blocks;
-    a.head_groups = H / wpg;
-    a.waves_per_group = wpg;
+    a.head_groups = H / fw;
+    a.waves_per_group = fw;
     a.nr = plan.nr;
     a.max_chunk = plan.max_chunk;
-    e = pkv::launch_pa_decode_flat(a, D, wpg * 64, static_cast<hipStream_t>(stream));
+    a.keep_cached = keep_cached;
+    e = pkv::launch_pa_decode_flat(a, D, fw * 64, static_cast<hipStream_t>(stream));
   } else {
     const long long grid = (long long)B * (H / wpg) * (plan.max_parts > 0 ? plan.max_parts : 1);
     if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
@@ -194,6 +208,7 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
     a.max_parts = plan.max_parts;
     a.head_groups = H / wpg;
     a.waves_per_group = wpg;
+    a.keep_cached = keep_cached;
     e = pkv::launch_pa_decode(a, D, (int)grid, wpg * 64, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -206,7 +221,7 @@ int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
                   void* workspace, size_t workspace_bytes, void* stream) {
   return pkv_pa_decode_ex(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                           max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
-                          workspace_bytes, 0, stream);
+                          workspace_bytes, 0, 0u, stream);
 }
 
 int pkv_kv_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,

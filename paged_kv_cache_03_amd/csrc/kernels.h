@@ -28,6 +28,7 @@ struct PartArgs {
   int max_parts;       // partitions of the longest sequence
   int head_groups;     // H / waves_per_group
   int waves_per_group;
+  bool keep_cached;    // normal cache policy for the tiles (blocks shared)
 };
 
 struct MergeArgs {
@@ -49,6 +50,18 @@ struct MergeArgs {
 #ifndef PKV_FLAT_TILES
 #define PKV_FLAT_TILES 3
 #endif
+#ifndef PKV_FLAT_WAVES
+#define PKV_FLAT_WAVES 4
+#endif
+// Waves (heads) per flat workgroup.
+constexpr int kFlatMaxWaves = PKV_FLAT_WAVES;
+// Cache-policy bits of the K/V tile loads by default: non-temporal (NT) on
+// gfx950, i.e. tiles stream through the caches with low retention (batch 200:
+// 347 -> 313 us).  Callers whose tables share blocks ask for the normal
+// policy instead, so that shared blocks are found in L2 (shared 1024-token
+// prefix: 169 -> 134 us).
+constexpr int kStreamPolicy = 2;
+constexpr int kCachedPolicy = 0;
 // Workgroups of 4 waves resident at once (256 CUs x 2 at the flat kernel's
 // register use) and tiles in each wave's load ring.
 constexpr int kFlatGridTarget = PKV_FLAT_GRID;
@@ -64,6 +77,7 @@ struct FlatArgs {
   _Float16* out;
   float* ws_ml;        // [H][nr][2 pieces][2]: running max (log2 units), running sum
   float* ws_acc;       // [H][nr][2 pieces][D]: unnormalised weighted sums
+  int* ws_seq;         // [B + 1]: first position of each sequence, then T
   float scale_log2;
   int B, H;
   int max_blocks;
@@ -73,6 +87,7 @@ struct FlatArgs {
   int waves_per_group;
   int nr;              // ranges (workgroups) per head group
   int max_chunk;       // longest range, in blocks (LDS sizing)
+  bool keep_cached;    // normal cache policy for the tiles (blocks shared)
 };
 
 struct AppendArgs {

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace pkv {
 namespace dev {
 
@@ -131,14 +133,15 @@ struct Tile {
 
 // One (block, head) tile of K and of V through buffer resources covering
 // exactly the two tiles; `lane_off` = lane * 16.
-template <int D>
+// kPolicy: cache-policy bits of the loads (kStreamPolicy or 0).
+template <int D, int kPolicy>
 __device__ __forceinline__ void load_tile(Tile<D>& t, rsrc_t kr, rsrc_t vr, uint32_t lane_off) {
 #pragma unroll
   for (int i = 0; i < Geometry<D>::kLoads; ++i)
-    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * 1024, 0, 0);
+    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * 1024, 0, kPolicy);
 #pragma unroll
   for (int i = 0; i < Geometry<D>::kLoads; ++i)
-    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * 1024, 0, 0);
+    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * 1024, 0, kPolicy);
 }
 
 __device__ __forceinline__ h8v as_h8(u4v x) { return __builtin_bit_cast(h8v, x); }

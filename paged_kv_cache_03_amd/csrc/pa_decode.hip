@@ -30,7 +30,7 @@ namespace {
 
 using namespace dev;
 
-template <int D>
+template <int D, int kPolicy>
 __global__ __launch_bounds__(256) void pa_decode_part_kernel(PartArgs a) {
   constexpr int L = Geometry<D>::kLoads;
   constexpr int kAcc = Geometry<D>::kAcc;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void pa_decode_part_kernel(PartArgs a) {
   Tile<D> ta, tb;
   auto fetch = [&](Tile<D>& t, int j) {
     const size_t o = block_off(min(j, nb - 1));
-    load_tile<D>(t, make_rsrc(kpool + o, kTile), make_rsrc(vpool + o, kTile), lane_off);
+    load_tile<D, kPolicy>(t, make_rsrc(kpool + o, kTile), make_rsrc(vpool + o, kTile), lane_off);
   };
   fetch(ta, 0);
   int j = 0;
@@ -183,10 +183,14 @@ __global__ __launch_bounds__(256) void pa_decode_merge_kernel(MergeArgs a) {
 
 hipError_t launch_pa_decode(const PartArgs& part, int D, int grid_part, int threads,
                             hipStream_t stream) {
-  if (D == 128)
-    hipLaunchKernelGGL(pa_decode_part_kernel<128>, dim3(grid_part), dim3(threads), 0, stream, part);
+  if (D == 128 && !part.keep_cached)
+    hipLaunchKernelGGL((pa_decode_part_kernel<128, kStreamPolicy>), dim3(grid_part), dim3(threads), 0, stream, part);
+  else if (D == 128)
+    hipLaunchKernelGGL((pa_decode_part_kernel<128, kCachedPolicy>), dim3(grid_part), dim3(threads), 0, stream, part);
+  else if (!part.keep_cached)
+    hipLaunchKernelGGL((pa_decode_part_kernel<64, kStreamPolicy>), dim3(grid_part), dim3(threads), 0, stream, part);
   else
-    hipLaunchKernelGGL(pa_decode_part_kernel<64>, dim3(grid_part), dim3(threads), 0, stream, part);
+    hipLaunchKernelGGL((pa_decode_part_kernel<64, kCachedPolicy>), dim3(grid_part), dim3(threads), 0, stream, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || part.max_parts <= 1) return e;
   MergeArgs mg;

@@ -22,11 +22,14 @@
 //    result, at most two per wave ("head piece" = the range's first
 //    sequence begun earlier, "tail piece" = its last sequence going on
 //    later).  A second kernel merges the pieces of each cut sequence in
-//    ascending position order and writes zero rows for empty sequences.
+//    ascending position order and writes zero rows for empty sequences; the
+//    sequence offsets it needs are published by workgroup 0.
 //
 // Block ids of the workgroup's range are staged once in LDS (one gather for
-// all its waves); the per-sequence block offsets come from a prefix sum of
-// the context lengths, computed in LDS by every workgroup.
+// all its waves), each with its count of tokens in use; the per-sequence
+// block offsets come from a prefix sum of the context lengths, computed in
+// LDS by every workgroup.  The ring's loads past the end of the range
+// address a zero-size buffer resource, so they fetch nothing.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,6 +43,7 @@ namespace {
 using namespace dev;
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int limit) { return min(max(ctx, 0), limit); }
+
 
 // s_start[b] = blocks of the sequences before b (b <= B; s_start[B] = T);
 // s_tail[b] (if given) = tokens used in sequence b's last block.  All
@@ -132,17 +136,17 @@ __device__ __forceinline__ void store_acc(rsrc_t r, uint32_t off, const float (&
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void pa_decode_flat_kernel(FlatArgs a) {
+template <int D, int kPolicy>
+__global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(FlatArgs a) {
   constexpr int kAcc = Geometry<D>::kAcc;
   constexpr int kTile = Geometry<D>::kTileBytes;
   constexpr int kOut = Geometry<D>::kOutPerLane;
   extern __shared__ int smem[];
-  __shared__ int s_wave[4];
-  __shared__ uint32_t s_q[4][kWave];   // per-wave query staging
+  __shared__ int s_wave[kFlatMaxWaves];
+  __shared__ uint32_t s_q[kFlatMaxWaves][kWave];   // per-wave query staging
   int* s_start = smem;                 // B + 1
   int* s_tail = smem + a.B + 1;        // B
-  int* s_ids = smem + 2 * a.B + 1;     // up to max_chunk
+  int* s_ids = smem + 2 * a.B + 1;     // max_chunk block ids
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -154,12 +158,16 @@ __global__ __launch_bounds__(256) void pa_decode_flat_kernel(FlatArgs a) {
   const int h = g * a.waves_per_group + wave;
 
   block_prefix(a.context_lens, a.B, a.ctx_limit, s_start, s_tail, s_wave);
+  if (blockIdx.x == 0) {               // offsets for the merge kernel
+    for (int i = tid; i <= a.B; i += blockDim.x) a.ws_seq[i] = s_start[i];
+  }
   const int T = s_start[a.B];
   const int chunk = (T + a.nr - 1) / a.nr;
   const int c0 = min(T, r * chunk);
   const int c1 = min(T, c0 + chunk);
   if (c0 >= c1) return;                // uniform for the workgroup
 
+  // Physical block id of every position of the range.
   for (int s = c0 + tid; s < c1; s += blockDim.x) {
     const int b = seq_of(s_start, a.B, s);
     const int id = a.block_tables[(size_t)b * a.max_blocks + (s - s_start[b])];
@@ -171,10 +179,17 @@ __global__ __launch_bounds__(256) void pa_decode_flat_kernel(FlatArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
   const size_t block_stride = (size_t)a.H * kTile;
   const uint32_t lane_off = lane * 16u;
+  // Past the range's end the load ring still issues its loads (so the load
+  // counters stay exact) but through a zero-size resource: they return 0
+  // without touching memory.
+  // Past the range's end the load ring still issues its loads (so the load
+  // counters stay exact) but through a zero-size resource: they return 0
+  // without touching memory.
   auto fetch = [&](Tile<D>& t, int s) {
     const int j = min(s, c1 - 1) - c0;
+    const uint32_t bytes = s < c1 ? kTile : 0u;
     const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[j]) * block_stride;
-    load_tile<D>(t, make_rsrc(kbase + o, kTile), make_rsrc(vbase + o, kTile), lane_off);
+    load_tile<D, kPolicy>(t, make_rsrc(kbase + o, bytes), make_rsrc(vbase + o, bytes), lane_off);
   };
 
   // Current segment: sequence b, positions [seg_lo, seg_hi) of its
@@ -248,9 +263,7 @@ __global__ __launch_bounds__(256) void pa_decode_flat_kernel(FlatArgs a) {
   };
 
   // kFlatTiles tiles in rotation: while one is consumed the next
-  // kFlatTiles - 1 are in flight.  The prefetch index is clamped to the
-  // range's last block (re-reading it is an L1/L2 hit), so every iteration
-  // issues the same loads and the load counters stay exact.
+  // kFlatTiles - 1 are in flight; every iteration issues the same loads.
   Tile<D> t[kFlatTiles];
 #pragma unroll
   for (int k = 0; k + 1 < kFlatTiles; ++k) fetch(t[k], c0 + k);
@@ -268,48 +281,53 @@ __global__ __launch_bounds__(256) void pa_decode_flat_kernel(FlatArgs a) {
 done:;
 }
 
-// One workgroup per sequence: zero rows for an empty sequence; for a
-// sequence cut across ranges, merge its pieces (weights exp2(m_r - M)) in
-// ascending range order.
+// One wave per (sequence, head), four per workgroup.  Zero row for an empty
+// sequence; for a sequence cut across ranges, merge its pieces (weights
+// exp2(m_r - M)) in ascending range order; otherwise nothing (the decode
+// kernel wrote the row).  Sequence offsets come from the decode kernel
+// (ws_seq), so no prefix sum is redone here.
 template <int D>
 __global__ __launch_bounds__(256) void pa_decode_flat_merge_kernel(FlatArgs a) {
-  extern __shared__ int smem[];
-  __shared__ int s_wave[4];
-  int* s_start = smem;
-  block_prefix(a.context_lens, a.B, a.ctx_limit, s_start, nullptr, s_wave);
-  const int T = s_start[a.B];
-  const int chunk = (T + a.nr - 1) / a.nr;
-  const int b = blockIdx.x;
-  const int S = s_start[b];
-  const int E = s_start[b + 1];
-  const size_t out_row = (size_t)b * a.H * D;
+  constexpr int kPer = D / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int bh = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (bh >= a.B * a.H) return;
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int T = a.ws_seq[a.B];
+  const int S = a.ws_seq[b];
+  const int E = a.ws_seq[b + 1];
+  _Float16* orow = a.out + (size_t)bh * D;
   if (E == S) {
-    for (int i = threadIdx.x; i < a.H * D; i += blockDim.x) a.out[out_row + i] = (_Float16)0.0f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) orow[lane * kPer + k] = (_Float16)0.0f;
     return;
   }
+  const int chunk = (T + a.nr - 1) / a.nr;
   const int r0 = S / chunk;
   const int r1 = (E - 1) / chunk;
   if (r0 == r1) return;                // written whole by the decode kernel
-  for (int i = threadIdx.x; i < a.H * (D / 2); i += blockDim.x) {
-    const int h = i / (D / 2);
-    const int d = (i % (D / 2)) * 2;
-    float mx = kNegInf;
-    for (int rr = r0; rr <= r1; ++rr) {
-      const size_t piece = ((size_t)h * a.nr + rr) * 2 + (rr * chunk > S ? 0 : 1);
-      mx = fmaxf(mx, a.ws_ml[piece * 2]);
-    }
-    float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
-    for (int rr = r0; rr <= r1; ++rr) {
-      const size_t piece = ((size_t)h * a.nr + rr) * 2 + (rr * chunk > S ? 0 : 1);
-      const float w = exp2f(a.ws_ml[piece * 2] - mx);
-      den = fmaf(w, a.ws_ml[piece * 2 + 1], den);
-      n0 = fmaf(w, a.ws_acc[piece * D + d], n0);
-      n1 = fmaf(w, a.ws_acc[piece * D + d + 1], n1);
-    }
-    const float inv = 1.0f / den;
-    a.out[out_row + (size_t)h * D + d] = (_Float16)(n0 * inv);
-    a.out[out_row + (size_t)h * D + d + 1] = (_Float16)(n1 * inv);
+  auto piece = [&](int rr) {
+    return ((size_t)h * a.nr + rr) * 2 + (rr * chunk > S ? 0 : 1);
+  };
+  float mx = kNegInf;
+#pragma unroll 4
+  for (int rr = r0; rr <= r1; ++rr) mx = fmaxf(mx, a.ws_ml[piece(rr) * 2]);
+  float den = 0.0f;
+  float num[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) num[k] = 0.0f;
+#pragma unroll 4
+  for (int rr = r0; rr <= r1; ++rr) {
+    const size_t p = piece(rr);
+    const float w = exp2f(a.ws_ml[p * 2] - mx);
+    den = fmaf(w, a.ws_ml[p * 2 + 1], den);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) num[k] = fmaf(w, a.ws_acc[p * D + lane * kPer + k], num[k]);
   }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) orow[lane * kPer + k] = (_Float16)(num[k] * inv);
 }
 
 }  // namespace
@@ -321,17 +339,21 @@ size_t flat_lds_bytes(int B, int max_chunk) {
 hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream) {
   const size_t lds = flat_lds_bytes(a.B, a.max_chunk);
   const int grid = a.head_groups * a.nr;
-  if (D == 128)
-    hipLaunchKernelGGL(pa_decode_flat_kernel<128>, dim3(grid), dim3(threads), lds, stream, a);
+  if (D == 128 && !a.keep_cached)
+    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kStreamPolicy>), dim3(grid), dim3(threads), lds, stream, a);
+  else if (D == 128)
+    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kCachedPolicy>), dim3(grid), dim3(threads), lds, stream, a);
+  else if (!a.keep_cached)
+    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kStreamPolicy>), dim3(grid), dim3(threads), lds, stream, a);
   else
-    hipLaunchKernelGGL(pa_decode_flat_kernel<64>, dim3(grid), dim3(threads), lds, stream, a);
+    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kCachedPolicy>), dim3(grid), dim3(threads), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds_merge = (size_t)(a.B + 1) * sizeof(int);
+  const int merge_grid = (a.B * a.H + 3) / 4;
   if (D == 128)
-    hipLaunchKernelGGL(pa_decode_flat_merge_kernel<128>, dim3(a.B), dim3(256), lds_merge, stream, a);
+    hipLaunchKernelGGL(pa_decode_flat_merge_kernel<128>, dim3(merge_grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(pa_decode_flat_merge_kernel<64>, dim3(a.B), dim3(256), lds_merge, stream, a);
+    hipLaunchKernelGGL(pa_decode_flat_merge_kernel<64>, dim3(merge_grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ def default_partition(batch, num_heads, head_dim, max_context_len):
 
 
 def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
-              max_context_len=None, workspace=None, partition_tokens=0):
+              max_context_len=None, workspace=None, partition_tokens=0, keep_cached=False):
     """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the first
     context_lens[b] tokens of sequence b, read through block_tables[b].
 
@@ -72,7 +72,10 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
     [B][max_blocks] int32; context_lens: [B] int32.  ``max_context_len`` must
     be >= every context length; when omitted it is read back from the device
     (one synchronisation).  ``workspace``: a uint8 device tensor of at least
-    ``pa_decode_workspace_size(...)`` bytes, allocated here when omitted."""
+    ``pa_decode_workspace_size(...)`` bytes, allocated here when omitted.
+    ``keep_cached``: load K/V with the normal cache policy instead of
+    streaming it, for batches whose tables share blocks (see
+    ``blocks.tables_share_blocks``); the result is the same either way."""
     lib = _lib.load_library()
     _need(q, "q", torch.float16, ndim=3)
     dev = q.device
@@ -102,7 +105,8 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
         code = lib.pkv_pa_decode_ex(
             _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), max_context_len, B, H, D, BLOCK_TOKENS, NB, float(scale),
-            _ptr(out), _ptr(workspace), ws_bytes, partition_tokens, _stream_handle(dev))
+            _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
+            _lib.DECODE_KEEP_KV_CACHED if keep_cached else 0, _stream_handle(dev))
     _lib.check("pkv_pa_decode", code)
     return out
 

@@ -50,12 +50,13 @@ def test_status_strings(lib):
 
 def decode(lib, **kw):
     args = dict(q=A16, k=A16, v=A16, tables=A16, maxb=128, ctx=A16, maxctx=2048, B=4, H=32,
-                D=128, bs=16, nb=1024, scale=0.088, out=A16, ws=A16, wsb=1 << 30, part=0)
+                D=128, bs=16, nb=1024, scale=0.088, out=A16, ws=A16, wsb=1 << 30, part=0,
+                flags=0)
     args.update(kw)
     return lib.pkv_pa_decode_ex(args["q"], args["k"], args["v"], args["tables"], args["maxb"],
                                 args["ctx"], args["maxctx"], args["B"], args["H"], args["D"],
                                 args["bs"], args["nb"], args["scale"], args["out"], args["ws"],
-                                args["wsb"], args["part"], None)
+                                args["wsb"], args["part"], args["flags"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,6 +69,7 @@ def decode(lib, **kw):
     (dict(nb=0), _lib.ERR_BAD_SHAPE),
     (dict(part=24), _lib.ERR_BAD_SHAPE),
     (dict(part=1024), _lib.ERR_BAD_SHAPE),
+    (dict(flags=2), _lib.ERR_BAD_SHAPE),           # unknown flag bit
     (dict(q=None), _lib.ERR_NULL_PTR),
     (dict(k=None), _lib.ERR_NULL_PTR),
     (dict(tables=None), _lib.ERR_NULL_PTR),
@@ -100,7 +102,8 @@ def test_workspace_size(lib):
     flat = lib.pkv_pa_decode_workspace_size(B, H, D, ctx)
     assert 0 < flat < (16 << 20)
     assert lib.pkv_pa_decode_workspace_size(B, H, D, 1024) == flat
-    assert lib.pkv_pa_decode_workspace_size(10, H, D, ctx) == flat
+    # ... and only the per-sequence offsets (one int32 each) grow with the batch
+    assert flat - lib.pkv_pa_decode_workspace_size(10, H, D, ctx) == (B - 10) * 4
     # explicit partitions: one (m, l, acc[D]) slot per (sequence, head, partition)
     part = 256
     np_ = -(-ctx // part)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from paged_kv_cache_03_amd.blocks import (PagedRequest, PagePool, PoolExhausted, device_arrays,
-                                          kv_bytes_per_token)
+                                          kv_bytes_per_token, tables_share_blocks)
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
                                      "pages_worked_examples.json")))
@@ -192,3 +192,14 @@ def test_slots_follow_the_table():
     tables, lens = device_arrays([r, PagedRequest(pool)], width=5)
     assert tables.shape == (2, 5) and lens.tolist() == [50, 0]
     assert tables[0, :4].tolist() == r.block_table and (tables[0, 4:] == -1).all()
+
+
+def test_tables_share_blocks():
+    pool = PagePool(16)
+    a = PagedRequest(pool)
+    a.append_tokens(20)
+    b = PagedRequest(pool)
+    b.append_tokens(5)
+    assert not tables_share_blocks([a, b])
+    c = a.fork()
+    assert tables_share_blocks([b, c, a]) and not tables_share_blocks([c])

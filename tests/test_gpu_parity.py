@@ -19,11 +19,12 @@ from tests._gpu import assert_close, dev, device_pools, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(case, kp, vp, tables=None, partition=0):
+def run_decode(case, kp, vp, tables=None, partition=0, keep_cached=False):
     tables = case.block_tables if tables is None else tables
     q = to_dev(case.q)
     out = pa_decode(q, kp, vp, to_dev(tables), to_dev(case.context_lens), case.scale,
-                    max_context_len=case.max_context, partition_tokens=partition)
+                    max_context_len=case.max_context, partition_tokens=partition,
+                    keep_cached=keep_cached)
     torch.cuda.synchronize()
     return out
 
@@ -84,7 +85,7 @@ def test_edge_contexts(H, D, partition):
     counts (2- and 1-wave workgroups), NaN in every unread slot."""
     c = _edge_case(H, D, [0, 1, 15, 16, 17, 255, 256, 257, 2048, 33], seed=H + D + partition)
     kp, vp = device_pools(c)
-    out = run_decode(c, kp, vp, partition=partition)
+    out = run_decode(c, kp, vp, partition=partition, keep_cached=(H % 2 == 1))
     ref = oracle(c, c.k_pool, c.v_pool)
     assert_close(out, ref, f"edge H={H} D={D} part={partition}")
     assert not to_host(out)[0].any()          # empty context -> zero row
@@ -138,6 +139,10 @@ def test_shared_prefix_copy_on_write():
     out = run_decode(c, kp, vp)
     assert torch.equal(out, shared_out)
     assert_close(out, oracle(c, k_ref, v_ref), "shared prefix")
+    # the cache policy changes no bit, with either strategy
+    assert torch.equal(run_decode(c, kp, vp, keep_cached=True), out)
+    p256 = run_decode(c, kp, vp, partition=256)
+    assert torch.equal(run_decode(c, kp, vp, partition=256, keep_cached=True), p256)
 
 
 def test_shared_prefix_ending_inside_a_block():

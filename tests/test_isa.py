@@ -1,0 +1,114 @@
+"""Checks on the gfx950 assembly of the decode kernels (CPU only: hipcc
+cross-compiles).
+
+The decode loops stream K/V with several tiles in flight per wave.  A full
+drain of the vector-memory counter (s_waitcnt vmcnt(0)) inside a loop would
+stall every prefetch; the compiler inserts one whenever a register that an
+in-flight load or store still uses gets reused, so these checks guard the
+code shapes that avoid it.  They also pin register use and the absence of
+scratch (spill) memory.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from paged_kv_cache_03_amd import build as B
+
+hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+pytestmark = pytest.mark.skipif(not os.path.exists(hipcc), reason="hipcc not available")
+
+
+def device_asm(src, tmp_path, defines=()):
+    out = tmp_path / (os.path.basename(src) + ".s")
+    cmd = [hipcc, *B.HIPCC_FLAGS, *defines, "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, src), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernel_body(asm, name_part):
+    m = re.search(r"^(_Z\S*" + name_part + r"\S*):\s*;.*$", asm, re.M)
+    assert m, f"kernel {name_part} not found"
+    start = m.end()
+    end = asm.index("s_endpgm", start)
+    body = asm[start:asm.index(".Lfunc_end", start)]
+    return body
+
+
+def meta(asm, name_part, key):
+    sym = re.search(r"^(_Z\S*" + name_part + r"\S*):", asm, re.M).group(1)
+    block = asm[asm.index(f".name:           {sym}") - 2000:asm.index(f".name:           {sym}") + 2000]
+    return int(re.search(rf"\.{key}:\s+(\d+)", block).group(1))
+
+
+@pytest.fixture(scope="module")
+def flat_asm(tmp_path_factory):
+    return device_asm("pa_decode_flat.hip", tmp_path_factory.mktemp("isa"))
+
+
+@pytest.fixture(scope="module")
+def part_asm(tmp_path_factory):
+    return device_asm("pa_decode.hip", tmp_path_factory.mktemp("isa"))
+
+
+def tile_loops(body):
+    """{loop header: text of every block of that loop} for the loops that
+    issue 16-byte tile loads, from the compiler's loop annotations (a header
+    block says "Loop Header", member blocks say "in Loop: Header=BB..")."""
+    blocks = re.split(r"^(?=\.LBB\d+_\d+:)", body, flags=re.M)
+    loops = {}
+    for blk in blocks:
+        first = blk.split("\n", 2)
+        head = "\n".join(first[:2])
+        m = re.match(r"\.LBB(\d+_\d+):", blk)
+        if not m:
+            continue
+        if "Loop Header" in head:
+            key = "BB" + m.group(1)
+        else:
+            h = re.search(r"in Loop: Header=(BB\d+_\d+)", head)
+            if not h:
+                continue
+            key = h.group(1)
+        loops[key] = loops.get(key, "") + blk
+    return {k: v for k, v in loops.items() if "buffer_load_dwordx4" in v}
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("policy", [2, 0])
+def test_flat_loop_never_drains_loads(flat_asm, D, policy):
+    body = kernel_body(flat_asm, f"pa_decode_flat_kernelILi{D}ELi{policy}E")
+    loops = tile_loops(body)
+    assert loops, "no tile loop found"
+    for label, text in loops.items():
+        assert "vmcnt(0)" not in text, f"full load drain inside loop {label}"
+    # nor anywhere once blocks are being consumed
+    assert "vmcnt(0)" not in body[body.index("v_dot2"):]
+    # the tiles are fetched as 16-byte buffer loads, non-temporal by default
+    nt = re.search(r"buffer_load_dwordx4 .* offen( offset:\d+)? nt", body)
+    assert bool(nt) == (policy == 2)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("policy", [2, 0])
+def test_partition_loop_never_drains_loads(part_asm, D, policy):
+    body = kernel_body(part_asm, f"pa_decode_part_kernelILi{D}ELi{policy}E")
+    loops = tile_loops(body)
+    assert loops, "no tile loop found"
+    for label, text in loops.items():
+        assert "vmcnt(0)" not in text, f"full load drain inside loop {label}"
+
+
+def test_no_spills_and_register_budget(flat_asm, part_asm):
+    for asm, name in ((flat_asm, "pa_decode_flat_kernelILi128E"),
+                      (part_asm, "pa_decode_part_kernelILi128E")):
+        assert meta(asm, name, "vgpr_spill_count") == 0
+        assert meta(asm, name, "private_segment_fixed_size") == 0
+    # two waves per SIMD for the flat kernel (<= 256 VGPRs), three for the
+    # partitioned one (<= 168)
+    assert meta(flat_asm, "pa_decode_flat_kernelILi128E", "vgpr_count") <= 256
+    assert meta(part_asm, "pa_decode_part_kernelILi128E", "vgpr_count") <= 168
