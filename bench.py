@@ -44,6 +44,12 @@ def parse():
                     help="sequences in the oracle sample (0 = sized to ~15 s)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic record from two rocprofv3 counter_collection "
+                         "CSVs (FETCH_SIZE pass, WRITE_SIZE pass; both runs with --copy-probe) "
+                         "and exit; needs no GPU")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the HBM read probes (achievable-bandwidth references)")
     return ap.parse_args()
 
 
@@ -57,15 +63,45 @@ def algorithmic_bytes(lens, H, D):
     return kv, kv + qo + tab
 
 
+def hbm_probe(torch, dev, nbytes=2 << 30):
+    """Achievable HBM read rates next to the 8 TB/s published peak: a plain
+    linear read, and a gather of 4 KiB chunks in random order (the decode's
+    pattern: one head's 16-token block, scattered over the pool), each the
+    best over a few grid sizes."""
+    import numpy as np
+    from paged_kv_cache_03_amd.ops import hbm_gather_probe, hbm_read_probe
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    chunk = 4096
+    perm = np.random.default_rng(0).permutation(nbytes // chunk).astype(np.int32)
+    order = torch.from_numpy(perm).to(dev)
+
+    def rate(call):
+        for _ in range(2):
+            call()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(10):
+            call()
+        e.record()
+        torch.cuda.synchronize()
+        return nbytes / (s.elapsed_time(e) / 10 / 1e3) / 1e9
+
+    lin = max((rate(lambda: hbm_read_probe(buf, sink, w)), w) for w in (256, 512, 1024, 2048))
+    gat = max((rate(lambda: hbm_gather_probe(buf, order, chunk, sink, w)), w) for w in (512, 1024))
+    del buf, order
+    return {"bytes": nbytes, "linear_gbs": round(lin[0], 1), "linear_workgroups": lin[1],
+            "gather_4k_gbs": round(gat[0], 1), "gather_workgroups": gat[1]}
+
+
 def kernel_source_sha256():
-    """Hash of the kernel sources and the C header, to tell whether stored
-    counter figures still describe the code that runs."""
-    import glob
+    """Hash of the sources the pa_decode call is built from (kernels, shared
+    device code, launch plan), to tell whether stored counter figures still
+    describe the code that runs."""
     import hashlib
     h = hashlib.sha256()
-    rels = sorted(glob.glob(os.path.join("paged_kv_cache_03_amd", "csrc", "*.hip"), root_dir=ROOT) +
-                  glob.glob(os.path.join("paged_kv_cache_03_amd", "csrc", "*.h"), root_dir=ROOT))
-    for rel in rels + [os.path.join("include", "pagedkv.h")]:
+    for name in ("api.hip", "pa_common.h", "pa_decode.hip", "pa_decode_flat.hip"):
+        rel = os.path.join("paged_kv_cache_03_amd", "csrc", name)
         h.update(rel.encode())
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
@@ -84,6 +120,50 @@ def measured_traffic():
     if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return int(rec["pa_decode_hbm_bytes_per_call"])
+
+
+def counter_kib_by_kernel(path, counter):
+    """Values of ``counter`` (KiB per dispatch), listed by kernel name, from a
+    rocprofv3 counter_collection CSV."""
+    import csv
+    vals = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def write_traffic_record(fetch_csv, write_csv, workload="batch200_append_seed2"):
+    """HBM bytes per pa_decode call (decode + merge kernels) from the two
+    counter passes, each scaled by what the same counter reads for the 1 GiB
+    device copy of --copy-probe (bytes moved / counter bytes), stored with the
+    hash of the kernel sources it describes."""
+    n = 1 << 30
+    rec = {"workload": workload, "kernel_source_sha256": kernel_source_sha256()}
+    total = 0
+    for which, path, counter in (("read", fetch_csv, "FETCH_SIZE"),
+                                 ("write", write_csv, "WRITE_SIZE")):
+        vals = counter_kib_by_kernel(path, counter)
+        mean = lambda xs: sum(xs) / len(xs)
+        # the 1 GiB copies, not the small host-to-device copies of the inputs
+        copies = [v for k, xs in vals.items() if "copyBuffer" in k for v in xs]
+        copies = [v for v in copies if v >= 0.5 * max(copies, default=0.0)]
+        dec = [xs for k, xs in vals.items() if "pa_decode_flat_kernel" in k]
+        mrg = [xs for k, xs in vals.items() if "pa_decode_flat_merge_kernel" in k]
+        if not copies or len(dec) != 1 or len(mrg) != 1:
+            raise SystemExit(f"{path}: expected the copy probe, one decode and one merge kernel")
+        factor = n / (mean(copies) * 1024)
+        b = int(round((mean(dec[0]) + mean(mrg[0])) * 1024 * factor))
+        rec[f"{which}_bytes"] = b
+        rec[f"{counter.lower()}_factor"] = round(factor, 4)
+        total += b
+    rec["pa_decode_hbm_bytes_per_call"] = total
+    rec["source"] = "pa_decode_flat_batch200_hbm_counters.md"
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(case, kp, vp, torch, budget_s=15.0, nseq=0):
@@ -265,6 +345,9 @@ def setup_full_step(torch, dev, wl, args, beams):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic_record(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
               "(every GPU box here has one).", file=sys.stderr)
@@ -346,6 +429,12 @@ def main():
         },
     }
     result.update(run.extra)
+
+    if not args.no_hbm_probe and args.workload == "batch200":
+        probe = hbm_probe(torch, dev)
+        result["hbm_probe"] = probe
+        result["roofline"]["achievable_gather_gbs"] = probe["gather_4k_gbs"]
+        result["roofline"]["frac_of_achievable"] = round(achieved / probe["gather_4k_gbs"], 4)
 
     if args.copy_probe:
         n = 1 << 30

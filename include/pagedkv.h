@@ -182,6 +182,29 @@ int pkv_cow_copy_blocks(void* const* k_pools, void* const* v_pools,
                         int32_t n_pairs, int32_t num_blocks, int64_t block_bytes,
                         void* stream);
 
+/*
+ * Measurement aids, not part of the decode path.  Each reads `bytes` (a
+ * multiple of 16) of device memory `buf` with 16-byte non-temporal loads
+ * from `workgroups` workgroups of 256 threads, asynchronously on `stream`,
+ * and stores nothing in practice (`sink`, 4 device bytes, is written only
+ * for a data pattern that does not occur).  Their timings are the HBM read
+ * rates plain reads reach on this GPU, the references for the decode
+ * kernel's block reads.
+ *
+ * pkv_hbm_read_probe: one linear pass over the buffer.
+ *
+ * pkv_hbm_gather_probe: the buffer as `bytes / chunk_bytes` chunks
+ * (`chunk_bytes` a power of two from 1 KiB to 1 MiB dividing `bytes`), read
+ * whole in the order of `chunk_order` (device int32, one entry per chunk;
+ * entries are clamped into range), 16 KiB in flight per wave.  A random
+ * permutation of 4 KiB chunks is the access pattern of 16-token blocks of
+ * one 128-dim head scattered over a pool.
+ */
+int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t workgroups,
+                       void* stream);
+int pkv_hbm_gather_probe(const void* buf, size_t bytes, const int32_t* chunk_order,
+                         int32_t chunk_bytes, void* sink, int32_t workgroups, void* stream);
+
 /* Static description of a status code. */
 const char* pkv_status_string(int code);
 

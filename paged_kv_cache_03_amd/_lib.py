@@ -39,6 +39,8 @@ SIGNATURES = {
     "pkv_kv_append": (_c.c_int, [_vp, _vp, _i32p, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pkv_cow_copy_blocks": (_c.c_int, [_c.POINTER(_vp), _c.POINTER(_vp), _i32, _i32p, _i32, _i32,
                                        _c.c_int64, _vp]),
+    "pkv_hbm_read_probe": (_c.c_int, [_vp, _c.c_size_t, _vp, _i32, _vp]),
+    "pkv_hbm_gather_probe": (_c.c_int, [_vp, _c.c_size_t, _i32p, _i32, _vp, _i32, _vp]),
     "pkv_status_string": (_c.c_char_p, [_c.c_int]),
     "pkv_abi_version": (_i32, []),
 }

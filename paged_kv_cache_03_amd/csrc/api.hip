@@ -280,4 +280,30 @@ int pkv_cow_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_
   return PKV_OK;
 }
 
+int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t workgroups,
+                       void* stream) {
+  if (bytes == 0 || bytes % 16 || workgroups <= 0) return PKV_ERR_BAD_SHAPE;
+  if (!buf || !sink) return PKV_ERR_NULL_PTR;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return PKV_ERR_MISALIGNED;
+  const hipError_t e = pkv::launch_hbm_read_probe(buf, (long long)(bytes / 16),
+                                                  static_cast<uint32_t*>(sink), workgroups,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_hbm_gather_probe(const void* buf, size_t bytes, const int32_t* chunk_order,
+                         int32_t chunk_bytes, void* sink, int32_t workgroups, void* stream) {
+  int log_kib = -1;
+  for (int k = 0; k <= 10; ++k)
+    if (chunk_bytes == (1 << (10 + k))) log_kib = k;
+  if (bytes == 0 || log_kib < 0 || bytes % (size_t)chunk_bytes || workgroups <= 0)
+    return PKV_ERR_BAD_SHAPE;
+  if (!buf || !chunk_order || !sink) return PKV_ERR_NULL_PTR;
+  if (!aligned(buf, 16) || !aligned(chunk_order, 4) || !aligned(sink, 4)) return PKV_ERR_MISALIGNED;
+  const hipError_t e = pkv::launch_hbm_gather_probe(
+      buf, chunk_order, (long long)(bytes / (size_t)chunk_bytes), log_kib,
+      static_cast<uint32_t*>(sink), workgroups, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // extern "C"

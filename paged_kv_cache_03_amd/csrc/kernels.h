@@ -116,6 +116,10 @@ hipError_t launch_pa_decode(const PartArgs& part, int D, int grid_part, int thre
                             hipStream_t stream);
 hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream);
 size_t flat_lds_bytes(int B, int max_chunk);
+hipError_t launch_hbm_read_probe(const void* buf, long long n16, uint32_t* sink, int grid,
+                                 hipStream_t stream);
+hipError_t launch_hbm_gather_probe(const void* buf, const int32_t* order, long long n_chunks,
+                                   int log_kib, uint32_t* sink, int grid, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_cow_copy(const CowArgs& a, hipStream_t stream);
 

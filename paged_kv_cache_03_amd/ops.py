@@ -162,3 +162,33 @@ def cow_copy_blocks(src_dst_pairs, k_pools, v_pools):
                                        src_dst_pairs.shape[0], NB, block_bytes,
                                        _stream_handle(dev))
     _lib.check("pkv_cow_copy_blocks", code)
+
+
+def hbm_read_probe(buf, sink, workgroups=2048):
+    """Read the whole of ``buf`` (a device tensor of a multiple of 16 bytes)
+    once, linearly, with non-temporal loads (measurement aid; see
+    pkv_hbm_read_probe).  ``sink``: a 4-byte-or-larger device tensor."""
+    lib = _lib.load_library()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    with torch.cuda.device(buf.device):
+        code = lib.pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                      workgroups, _stream_handle(buf.device))
+    _lib.check("pkv_hbm_read_probe", code)
+
+
+def hbm_gather_probe(buf, order, chunk_bytes, sink, workgroups=512):
+    """Read ``buf`` as chunks of ``chunk_bytes`` in the order of ``order``
+    (int32 device tensor, one entry per chunk); measurement aid, see
+    pkv_hbm_gather_probe."""
+    lib = _lib.load_library()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _need(order, "order", torch.int32, buf.device, ndim=1)
+    if chunk_bytes <= 0 or nbytes % chunk_bytes or order.numel() != nbytes // chunk_bytes:
+        raise ValueError("order must have one entry per chunk of buf")
+    with torch.cuda.device(buf.device):
+        code = lib.pkv_hbm_gather_probe(_ptr(buf), nbytes, _ptr(order), chunk_bytes, _ptr(sink),
+                                        workgroups, _stream_handle(buf.device))
+    _lib.check("pkv_hbm_gather_probe", code)

@@ -168,6 +168,23 @@ def test_cow_rejects_bad_arguments(lib):
     assert lib.pkv_cow_copy_blocks(None, None, 2, A16, 3, 64, 131072, None) == _lib.ERR_NULL_PTR
 
 
+def test_probe_rejects_bad_arguments(lib):
+    assert lib.pkv_hbm_read_probe(A16, 0, A16, 64, None) == _lib.ERR_BAD_SHAPE
+    assert lib.pkv_hbm_read_probe(A16, 24, A16, 64, None) == _lib.ERR_BAD_SHAPE
+    assert lib.pkv_hbm_read_probe(A16, 32, A16, 0, None) == _lib.ERR_BAD_SHAPE
+    assert lib.pkv_hbm_read_probe(None, 32, A16, 64, None) == _lib.ERR_NULL_PTR
+    assert lib.pkv_hbm_read_probe(A4, 32, A16, 64, None) == _lib.ERR_MISALIGNED
+    g = lib.pkv_hbm_gather_probe
+    assert g(A16, 0, A16, 4096, A16, 64, None) == _lib.ERR_BAD_SHAPE
+    assert g(A16, 8192, A16, 3072, A16, 64, None) == _lib.ERR_BAD_SHAPE    # not a power of two
+    assert g(A16, 8192, A16, 512, A16, 64, None) == _lib.ERR_BAD_SHAPE     # below 1 KiB
+    assert g(A16, 8192, A16, 2 << 20, A16, 64, None) == _lib.ERR_BAD_SHAPE  # above 1 MiB
+    assert g(A16, 6144, A16, 4096, A16, 64, None) == _lib.ERR_BAD_SHAPE    # not a whole chunk
+    assert g(A16, 8192, A16, 4096, A16, 0, None) == _lib.ERR_BAD_SHAPE
+    assert g(A16, 8192, None, 4096, A16, 64, None) == _lib.ERR_NULL_PTR
+    assert g(A4, 8192, A16, 4096, A16, 64, None) == _lib.ERR_MISALIGNED
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LibraryMissing):
