@@ -11,6 +11,6 @@ copy pairs.
 
 from ._lib import LIB_PATH, LibraryMissing, PagedKVError, load_library  # noqa: F401
 from .blocks import (PAGE_TOKENS, PagedRequest, PagePool, PoolExhausted,  # noqa: F401
-                     device_arrays, kv_bytes_per_token, tables_share_blocks)
+                     decode_groups, device_arrays, kv_bytes_per_token, tables_share_blocks)
 from .ops import (cow_copy_blocks, default_partition, kv_append, pa_decode,  # noqa: F401
                   pa_decode_workspace_size, pool_shape)

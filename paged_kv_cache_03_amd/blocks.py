@@ -196,6 +196,46 @@ def tables_share_blocks(requests):
     return False
 
 
+def decode_groups(requests, max_group=16):
+    """Arrange a batch for the grouped decode: requests whose tables start
+    with the same physical page (forks of one prompt, beams of one request)
+    are put next to each other, in first-seen order, and cut into groups of
+    at most ``max_group``.
+
+    Returns (order, group_offsets, shared_blocks): ``order`` lists request
+    indices in their new batch order; group g is order[group_offsets[g] :
+    group_offsets[g+1]]; ``shared_blocks[g]`` is the number of leading pages
+    every member of g maps to the same physical pages, counting only pages
+    that are full for every member (a page still being written belongs to
+    one holder after its copy-on-write)."""
+    if max_group <= 0:
+        raise ValueError("max_group must be positive")
+    buckets, keys = {}, []
+    for i, r in enumerate(requests):
+        key = r.block_table[0] if r.block_table else ("private", i)
+        if key not in buckets:
+            buckets[key] = []
+            keys.append(key)
+        buckets[key].append(i)
+    order, offsets, shared = [], [0], []
+    for key in keys:
+        members = buckets[key]
+        for c in range(0, len(members), max_group):
+            chunk = [requests[i] for i in members[c:c + max_group]]
+            s = min(r.num_tokens // r.pool.page_tokens for r in chunk)
+            first = chunk[0].block_table
+            for r in chunk[1:]:
+                k = 0
+                while k < s and r.block_table[k] == first[k]:
+                    k += 1
+                s = k
+            order.extend(members[c:c + max_group])
+            offsets.append(len(order))
+            shared.append(s)
+    return (np.array(order, dtype=np.int64), np.array(offsets, dtype=np.int32),
+            np.array(shared, dtype=np.int32))
+
+
 def device_arrays(requests, width=None):
     """Block tables ([B][width] int32, -1 padded) and context lengths ([B]
     int32) for a batch of requests."""
