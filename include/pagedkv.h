@@ -183,6 +183,61 @@ int pkv_cow_copy_blocks(void* const* k_pools, void* const* v_pools,
                         void* stream);
 
 /*
+ * Decode for groups of sequences that share leading blocks: the branches of
+ * parallel sampling or beam search, requests forked from one prompt
+ * ("PagedAttention", e-fortepiano.pl, "Descripció": physical blocks shared
+ * between requests and decoding branches through the block tables; "Atención
+ * paginada ...", 7minutos.es, prefix-sharing part: a fork shares its owner's
+ * pages, and a page is copied before a holder writes into it, so the pages
+ * still shared are full pages at the front of the tables).
+ *
+ * Every output row is the single-query decode of pkv_pa_decode for that
+ * sequence (same formula, fp32 arithmetic, fp16 output); a shared block is
+ * read once for all members of its group, and the score and value products
+ * of a tile run on the matrix cores for all members at once (probabilities
+ * enter the value product rounded to fp16, so results match pkv_pa_decode
+ * to rounding, not bit for bit).
+ *
+ * Grouping (device int32 arrays, read as follows):
+ *   group g, 0 <= g < num_groups, holds the consecutive sequences
+ *   [group_offsets[g], group_offsets[g+1]) (offsets clamped into [0, B],
+ *   non-decreasing; a group with a negative size is empty); only its first
+ *   group_size members are decoded;
+ *   the group's first group_shared_blocks[g] logical blocks, clamped into
+ *   [0, min over its decoded members of context_lens/16], are read through
+ *   the table row of its first member for every member (so they must be the
+ *   same physical blocks, or blocks holding the same data, in every
+ *   member's table).
+ * Sequences in no group, members past group_size and sequences with
+ * context 0 get zero rows.  Overlapping groups are a caller error (rows
+ * unspecified, no access out of bounds).
+ *
+ * device: q, k_pool, v_pool, out (16-byte aligned), block_tables,
+ *         context_lens, group_offsets (num_groups + 1 entries),
+ *         group_shared_blocks (num_groups entries), workspace (256-byte
+ *         aligned, at least pkv_pa_decode_grouped_workspace_size bytes).
+ * host:   num_groups >= 0 (at most 12287); 1 <= group_size <= 16; the
+ *         other sizes, block_size, max_context_len and flags as for
+ *         pkv_pa_decode_ex (PKV_DECODE_KEEP_KV_CACHED is accepted; shared
+ *         blocks are read once either way).
+ * The workspace holds intermediate results only (no initialisation needed).
+ */
+int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len,
+                          const int32_t* group_offsets, const int32_t* group_shared_blocks,
+                          int32_t num_groups, int32_t group_size,
+                          int32_t B, int32_t H, int32_t D, int32_t block_size,
+                          int32_t num_blocks, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, uint32_t flags,
+                          void* stream);
+
+/* Workspace bytes for pkv_pa_decode_grouped (0 for invalid sizes or B = 0). */
+size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,
+                                            int32_t max_context_len, int32_t num_groups,
+                                            int32_t group_size);
+
+/*
  * Measurement aids, not part of the decode path.  Each reads `bytes` (a
  * multiple of 16) of device memory `buf` with 16-byte non-temporal loads
  * from `workgroups` workgroups of 256 threads, asynchronously on `stream`,

@@ -96,6 +96,40 @@ bool decode_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx) {
          (long long)B * H <= (1LL << 26);
 }
 
+// Grouped decode: workspace = per-sequence map, then (m, l) and acc of every
+// (partition, member slot, head).  Partitions are bounded without looking at
+// device data: a group's partitions number at most its positions / part + 1,
+// and its positions at most the blocks of its members, so all groups together
+// have at most ceil(B * max_blocks / part) + G partitions.
+struct GroupPlan {
+  int32_t max_parts = 0;
+  size_t map_bytes = 0;
+  size_t ml_bytes = 0;
+  size_t total = 0;
+};
+
+bool group_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t G,
+                    int32_t group_size) {
+  return decode_shape_ok(B, H, D, max_ctx) && G >= 0 &&
+         pkv::grouped_lds_bytes(G) <= (size_t)pkv::kGroupMaxLdsBytes && group_size >= 1 &&
+         group_size <= pkv::kGroupMaxMembers &&
+         (long long)B * H * D * 2 < (1LL << 32);
+}
+
+GroupPlan make_group_plan(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t G,
+                          int32_t group_size) {
+  GroupPlan p;
+  const long long parts =
+      ((long long)B * ceil_div(max_ctx, kBlockTokens) + pkv::kGroupPartBlocks - 1) /
+          pkv::kGroupPartBlocks + G;
+  p.max_parts = (int32_t)(parts < (1LL << 30) ? parts : (1LL << 30));
+  const size_t pieces = (size_t)p.max_parts * group_size * H;
+  p.map_bytes = round_up((size_t)B * 2 * sizeof(int32_t), kWsAlign);
+  p.ml_bytes = round_up(pieces * 2 * sizeof(float), kWsAlign);
+  p.total = p.map_bytes + p.ml_bytes + pieces * D * sizeof(float);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,6 +256,72 @@ int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
   return pkv_pa_decode_ex(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                           max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
                           workspace_bytes, 0, 0u, stream);
+}
+
+size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,
+                                            int32_t max_context_len, int32_t num_groups,
+                                            int32_t group_size) {
+  if (!group_shape_ok(B, H, D, max_context_len, num_groups, group_size) || B == 0) return 0;
+  return make_group_plan(B, H, D, max_context_len, num_groups, group_size).total;
+}
+
+int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len,
+                          const int32_t* group_offsets, const int32_t* group_shared_blocks,
+                          int32_t num_groups, int32_t group_size, int32_t B, int32_t H,
+                          int32_t D, int32_t block_size, int32_t num_blocks, float scale,
+                          void* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                          void* stream) {
+  if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)PKV_DECODE_KEEP_KV_CACHED) return PKV_ERR_BAD_SHAPE;
+  if (!group_shape_ok(B, H, D, max_context_len, num_groups, group_size)) return PKV_ERR_BAD_SHAPE;
+  if (B == 0) return PKV_OK;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      (long long)max_blocks_per_seq * kBlockTokens < max_context_len)
+    return PKV_ERR_BAD_SHAPE;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PKV_ERR_NULL_PTR;
+  if (num_groups > 0 && (!group_offsets || !group_shared_blocks)) return PKV_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(group_offsets, 4) ||
+      !aligned(group_shared_blocks, 4))
+    return PKV_ERR_MISALIGNED;
+  const GroupPlan plan = make_group_plan(B, H, D, max_context_len, num_groups, group_size);
+  if (!workspace) return PKV_ERR_NULL_PTR;
+  if (!aligned(workspace, kWsAlign)) return PKV_ERR_MISALIGNED;
+  if (workspace_bytes < plan.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+
+  pkv::GroupArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.group_offsets = group_offsets;
+  a.group_shared = group_shared_blocks;
+  a.out = static_cast<_Float16*>(out);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_map = reinterpret_cast<int*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.map_bytes);
+  a.ws_acc = reinterpret_cast<float*>(ws + plan.map_bytes + plan.ml_bytes);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.B = B;
+  a.H = H;
+  a.G = num_groups;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_limit = max_context_len;
+  a.num_blocks = num_blocks;
+  a.group_size = group_size;
+  a.part_blocks = pkv::kGroupPartBlocks;
+  a.max_parts = plan.max_parts;
+  a.head_groups = (H + pkv::kGroupWaves - 1) / pkv::kGroupWaves;
+  a.keep_cached = (flags & PKV_DECODE_KEEP_KV_CACHED) != 0;
+  // workgroup 0 always runs: it writes the per-sequence map the merge reads
+  const long long items = (long long)plan.max_parts * a.head_groups;
+  const int grid = (int)(items < pkv::kGroupGridTarget ? (items > 0 ? items : 1)
+                                                        : pkv::kGroupGridTarget);
+  const hipError_t e = pkv::launch_pa_decode_grouped(a, D, grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 int pkv_kv_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,

@@ -90,6 +90,40 @@ struct FlatArgs {
   bool keep_cached;    // normal cache policy for the tiles (blocks shared)
 };
 
+// Grouped decode (pa_decode_grouped.hip): groups of up to kGroupMaxMembers
+// sequences sharing leading blocks; one MFMA column per member.
+constexpr int kGroupMaxMembers = 16;
+constexpr int kGroupWaves = 4;             // waves (heads) per workgroup
+constexpr int kGroupTiles = 3;             // tiles in each wave's load ring
+constexpr int kMaxGroupPartBlocks = 64;    // longest partition, in positions (blocks)
+constexpr int kGroupPartBlocks = 32;       // partition length the launch plan asks for
+constexpr int kGroupGridTarget = 1024;     // workgroups launched at most (grid-stride loop)
+constexpr int kGroupMaxLdsBytes = 48 * 1024;
+
+struct GroupArgs {
+  const _Float16* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* group_offsets;  // [G + 1]: group g = sequences [off[g], off[g+1])
+  const int32_t* group_shared;   // [G]: leading blocks the members share
+  _Float16* out;
+  int* ws_map;         // [B][2]: first partition of the sequence's group, partitions*16 + member
+  float* ws_ml;        // [max_parts][group_size][H][2]: running max (log2 units), running sum
+  float* ws_acc;       // [max_parts][group_size][H][D]: unnormalised weighted sums
+  float scale_log2;
+  int B, H, G;
+  int max_blocks;
+  int ctx_limit;
+  int num_blocks;
+  int group_size;      // members decoded per group (1..kGroupMaxMembers)
+  int part_blocks;     // partition length (positions) target
+  int max_parts;       // workspace capacity in partitions
+  int head_groups;     // ceil(H / kGroupWaves)
+  bool keep_cached;
+};
+
 struct AppendArgs {
   const void* k;
   const void* v;
@@ -120,6 +154,8 @@ hipError_t launch_hbm_read_probe(const void* buf, long long n16, uint32_t* sink,
                                  hipStream_t stream);
 hipError_t launch_hbm_gather_probe(const void* buf, const int32_t* order, long long n_chunks,
                                    int log_kib, uint32_t* sink, int grid, hipStream_t stream);
+hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, int grid, hipStream_t stream);
+size_t grouped_lds_bytes(int G);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_cow_copy(const CowArgs& a, hipStream_t stream);
 

@@ -111,6 +111,61 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
     return out
 
 
+def pa_decode_grouped_workspace_size(batch, num_heads, head_dim, max_context_len, num_groups,
+                                     group_size=16):
+    return int(_lib.load_library().pkv_pa_decode_grouped_workspace_size(
+        batch, num_heads, head_dim, max_context_len, num_groups, group_size))
+
+
+def pa_decode_grouped(q, k_pool, v_pool, block_tables, context_lens, group_offsets,
+                      shared_blocks, scale, out=None, *, max_context_len=None, group_size=16,
+                      workspace=None, keep_cached=False):
+    """``pa_decode`` for a batch arranged in groups of sequences that share
+    leading blocks (see ``blocks.decode_groups``): group g is sequences
+    [group_offsets[g], group_offsets[g+1]) and its first shared_blocks[g]
+    logical blocks are read once for all its members.  ``group_offsets``
+    ([G+1]) and ``shared_blocks`` ([G]) are int32 device tensors; the other
+    arguments are as for ``pa_decode``."""
+    lib = _lib.load_library()
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    B, H, D = q.shape
+    NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
+    if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
+        raise ValueError("k_pool and v_pool differ in size")
+    _need(block_tables, "block_tables", torch.int32, dev, ndim=2)
+    _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
+    _need(group_offsets, "group_offsets", torch.int32, dev, ndim=1)
+    _need(shared_blocks, "shared_blocks", torch.int32, dev, ndim=1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens do not match the batch")
+    G = shared_blocks.shape[0]
+    if group_offsets.shape[0] != G + 1:
+        raise ValueError("group_offsets must have one entry more than shared_blocks")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, dev, ndim=3)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B][H][D]")
+    need = pa_decode_grouped_workspace_size(B, H, D, max_context_len, G, group_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+        ws_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        code = lib.pkv_pa_decode_grouped(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), max_context_len, _ptr(group_offsets), _ptr(shared_blocks), G,
+            group_size, B, H, D, BLOCK_TOKENS, NB, float(scale), _ptr(out), _ptr(workspace),
+            ws_bytes, _lib.DECODE_KEEP_KV_CACHED if keep_cached else 0, _stream_handle(dev))
+    _lib.check("pkv_pa_decode_grouped", code)
+    return out
+
+
 def kv_append(k, v, slot_mapping, k_pool, v_pool):
     """Write row t of k / v ([T][H][D] fp16) into slot slot_mapping[t]
     (block slot//16, position slot%16) of one layer's pools; negative slots

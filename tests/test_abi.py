@@ -189,3 +189,49 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LibraryMissing):
         _lib.load_library(str(tmp_path / "libpagedkv.so"))
+
+
+def test_grouped_rejects_bad_arguments(lib):
+    g = lib.pkv_pa_decode_grouped
+
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, tables=A16, mb=128, lens=A16, max_ctx=2048, offs=A16,
+                 shared=A16, G=3, gs=16, B=8, H=32, D=128, bs=16, NB=64, scale=0.1, out=A16,
+                 ws=A16, ws_bytes=1 << 40, flags=0)
+        a.update(kw)
+        return g(a["q"], a["k"], a["v"], a["tables"], a["mb"], a["lens"], a["max_ctx"], a["offs"],
+                 a["shared"], a["G"], a["gs"], a["B"], a["H"], a["D"], a["bs"], a["NB"],
+                 a["scale"], a["out"], a["ws"], a["ws_bytes"], a["flags"], None)
+
+    assert call(bs=32) == _lib.ERR_UNSUPPORTED
+    assert call(flags=2) == _lib.ERR_BAD_SHAPE
+    assert call(gs=0) == _lib.ERR_BAD_SHAPE
+    assert call(gs=17) == _lib.ERR_BAD_SHAPE
+    assert call(G=-1) == _lib.ERR_BAD_SHAPE
+    assert call(G=1 << 20) == _lib.ERR_BAD_SHAPE            # prefix table does not fit LDS
+    assert call(D=96) == _lib.ERR_BAD_SHAPE
+    assert call(mb=100) == _lib.ERR_BAD_SHAPE               # table narrower than the context
+    assert call(B=0, q=None) == _lib.OK                      # empty batch: nothing to do
+    assert call(q=None) == _lib.ERR_NULL_PTR
+    assert call(offs=None) == _lib.ERR_NULL_PTR
+    assert call(shared=None) == _lib.ERR_NULL_PTR
+    assert call(ws=None) == _lib.ERR_NULL_PTR
+    assert call(out=A4) == _lib.ERR_MISALIGNED
+    assert call(ws=A16 + 16) == _lib.ERR_MISALIGNED
+    need = lib.pkv_pa_decode_grouped_workspace_size(8, 32, 128, 2048, 3, 16)
+    assert need > 0
+    assert call(ws_bytes=need - 1) == _lib.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_grouped_workspace_size():
+    lib = _lib.load_library()
+    ws = lib.pkv_pa_decode_grouped_workspace_size
+    assert ws(0, 32, 128, 2048, 0, 16) == 0
+    assert ws(8, 32, 128, 2048, 3, 0) == 0 and ws(8, 32, 128, 2048, -1, 16) == 0
+    # grows with every dimension it depends on
+    base = ws(200, 32, 128, 2048, 50, 4)
+    for bigger in (ws(400, 32, 128, 2048, 50, 4), ws(200, 64, 128, 2048, 50, 4),
+                   ws(200, 32, 128, 4096, 50, 4), ws(200, 32, 128, 2048, 50, 8),
+                   ws(200, 32, 128, 2048, 150, 4)):
+        assert bigger > base
+    assert ws(200, 32, 64, 2048, 50, 4) < base

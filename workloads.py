@@ -277,6 +277,35 @@ def full_step(batch=200, layers=32, context=MAX_SEQ, seed=4, heads=32, head_dim=
     return case
 
 
+def table_groups(tables, lens, max_group=16):
+    """Grouping arguments for a batch whose tables are given as arrays:
+    consecutive sequences whose first block is the same physical block form
+    a group (cut at ``max_group`` members); a group's shared count is the
+    number of leading blocks all its members map alike, limited to blocks
+    full for every member.  Returns (group_offsets [G+1], shared_blocks [G])
+    as int32 arrays."""
+    tables = np.asarray(tables)
+    lens = np.asarray(lens)
+    B = len(lens)
+    offs, shared = [0], []
+    b = 0
+    while b < B:
+        e = b + 1
+        while (e < B and e - b < max_group and lens[b] > 0 and lens[e] > 0
+               and tables[e, 0] == tables[b, 0]):
+            e += 1
+        s = int(min(lens[b:e]) // BLOCK)
+        for r in range(b + 1, e):
+            k = 0
+            while k < s and tables[r, k] == tables[b, k]:
+                k += 1
+            s = k
+        offs.append(e)
+        shared.append(s)
+        b = e
+    return np.array(offs, dtype=np.int32), np.array(shared, dtype=np.int32)
+
+
 def device_pool(torch, case, layer, which, device):
     """Fill one layer's K (which=0) or V (which=1) pool on ``device`` with
     N(0,1) fp16 from a generator seeded by (seed, layer, which)."""
