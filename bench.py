@@ -44,6 +44,10 @@ def parse():
                     help="sequences in the oracle sample (0 = sized to ~15 s)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--decode", choices=["auto", "flat", "grouped"], default="auto",
+                    help="decode entry point: pa_decode (flat strategy unless --partition) or "
+                         "pa_decode_grouped (each shared block read once per group); auto = "
+                         "grouped for the workloads whose tables share blocks")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic record from two rocprofv3 counter_collection "
                          "CSVs (FETCH_SIZE pass, WRITE_SIZE pass; both runs with --copy-probe) "
@@ -249,6 +253,25 @@ def setup_batch(torch, dev, wl, args, batch, seed):
                        "partition_tokens": part, "seed": seed})
 
 
+def grouped_decoder(torch, dev, wl, case, max_ctx):
+    """pa_decode_grouped over the case's tables, grouped as they share blocks
+    (consecutive sequences with a common first block, at most 16 a group)."""
+    from paged_kv_cache_03_amd import pa_decode_grouped, pa_decode_grouped_workspace_size
+    offs, shared = wl.table_groups(case.block_tables, case.context_lens)
+    B, H, D = case.batch, case.num_heads, case.head_dim
+    ws = torch.empty(pa_decode_grouped_workspace_size(B, H, D, max_ctx, len(shared)),
+                     dtype=torch.uint8, device=dev)
+    offs_t = torch.from_numpy(offs).to(dev)
+    shared_t = torch.from_numpy(shared).to(dev)
+
+    def decode(q, kp, vp, tables, lens, out):
+        pa_decode_grouped(q, kp, vp, tables, lens, offs_t, shared_t, case.scale, out,
+                          max_context_len=max_ctx, workspace=ws)
+
+    info = {"groups": len(shared), "shared_blocks_per_group": sorted(set(shared.tolist()))}
+    return decode, info
+
+
 def setup_shared_prefix(torch, dev, wl, args):
     """One layer, 100 sequences sharing a 1024-token prefix; each step copies
     the prefix's last block per sequence (copy-on-write) and decodes."""
@@ -261,28 +284,38 @@ def setup_shared_prefix(torch, dev, wl, args):
     q, tables, lens, pairs = t(case.q), t(case.block_tables), t(case.context_lens), t(case.cow_pairs)
     out = torch.empty_like(q)
     max_ctx = case.max_context
-    ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, args.partition)),
-                     dtype=torch.uint8, device=dev)
     kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
     import numpy as np
     used = np.unique(case.block_tables[case.block_tables >= 0])
     unique_bytes = int(used.size) * H * 16 * D * 2 * 2
+    extra = {"unique_kv_bytes": unique_bytes}
+    if args.decode == "flat":
+        ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, args.partition)),
+                         dtype=torch.uint8, device=dev)
+
+        def decode(q, kp, vp, tables, lens, out):
+            pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
+                      workspace=ws, partition_tokens=args.partition, keep_cached=True)
+        extra.update(decode="pa_decode", keep_cached=True)
+        strategy = "flat" if not args.partition else "partitioned"
+    else:
+        decode, info = grouped_decoder(torch, dev, wl, case, max_ctx)
+        extra.update(decode="pa_decode_grouped", **info)
+        strategy = "grouped"
 
     def step(events):
         cow_copy_blocks(pairs, [kp], [vp])
         events.append(torch.cuda.Event(enable_timing=True))
         events[-1].record()
-        pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
-                  workspace=ws, partition_tokens=args.partition, keep_cached=True)
+        decode(q, kp, vp, tables, lens, out)
         events.append(torch.cuda.Event(enable_timing=True))
         events[-1].record()
 
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
-               algo_bytes=algo_bytes, strategy="flat" if not args.partition else "partitioned",
-               part=args.partition, extra={"unique_kv_bytes": unique_bytes, "keep_cached": True},
+               algo_bytes=algo_bytes, strategy=strategy, part=args.partition, extra=extra,
                config={"workload": "one layer, batch 100, a 1024-token prefix in 64 shared "
                                    "blocks + private suffix U[0,500]; per step copy-on-write of "
-                                   "the prefix's last block for each sequence + pa_decode",
+                                   "the prefix's last block for each sequence + decode",
                        "batch": B, "heads": H, "head_dim": D, "block_tokens": 16,
                        "context_tokens": case.kv_tokens(), "max_context": max_ctx,
                        "num_blocks": case.num_blocks, "seed": 3})
@@ -312,6 +345,15 @@ def setup_full_step(torch, dev, wl, args, beams):
                      dtype=torch.uint8, device=dev)
     kv_layer, algo_layer = algorithmic_bytes(case.context_lens, H, D)
     layer_pools = [pools[l % distinct] for l in range(L)]
+    grouped = beams > 1 and args.decode != "flat" or args.decode == "grouped"
+    if grouped:
+        decode, info = grouped_decoder(torch, dev, wl, case, 2048)
+        dec_extra = {"decode": "pa_decode_grouped", **info}
+    else:
+        def decode(q, kp, vp, tables, lens, out):
+            pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=2048,
+                      workspace=ws, partition_tokens=args.partition, keep_cached=beams > 1)
+        dec_extra = {"decode": "pa_decode", "keep_cached": beams > 1}
 
     def step(events):
         if pairs is not None:
@@ -321,8 +363,7 @@ def setup_full_step(torch, dev, wl, args, beams):
             kv_append(kn[l], vn[l], slots, kp, vp)
             events.append(torch.cuda.Event(enable_timing=True))
             events[-1].record()
-            pa_decode(qs[l], kp, vp, tables, lens, case.scale, out, max_context_len=2048,
-                      workspace=ws, partition_tokens=args.partition, keep_cached=beams > 1)
+            decode(qs[l], kp, vp, tables, lens, out)
             events.append(torch.cuda.Event(enable_timing=True))
             events[-1].record()
 
@@ -330,11 +371,12 @@ def setup_full_step(torch, dev, wl, args, beams):
     used = np.unique(case.block_tables)
     return Run(case=case, kp=pools[0][0], vp=pools[0][1], step=step, seqs_per_step=B * L,
                kv_bytes=kv_layer * L, algo_bytes=algo_layer,
-               strategy="flat" if not args.partition else "partitioned", part=args.partition,
-               extra={"layers": L, "distinct_layer_pools": distinct, "keep_cached": beams > 1,
-                      "unique_kv_bytes_per_layer": int(used.size) * H * 16 * D * 2 * 2},
+               strategy="grouped" if grouped else "flat" if not args.partition else "partitioned",
+               part=args.partition,
+               extra={"layers": L, "distinct_layer_pools": distinct, **dec_extra,
+                      "unique_kv_bytes": int(used.size) * H * 16 * D * 2 * 2},
                config={"workload": f"full decode step: {L} layers x batch {B} x 2048 tokens, "
-                                   "32 heads x 128 dims fp16; per layer kv_append + pa_decode"
+                                   "32 heads x 128 dims fp16; per layer kv_append + decode"
                                    + (f"; {beams}-beam groups sharing all but the last block, "
                                       "copy-on-write of the last block per beam" if beams > 1
                                       else ""),
@@ -429,6 +471,8 @@ def main():
         },
     }
     result.update(run.extra)
+    if "unique_kv_bytes" in run.extra:      # per decode call: each distinct block once
+        result["pa_decode_unique_kv_gbs"] = round(run.extra["unique_kv_bytes"] / dec_avg_s / 1e9, 2)
 
     if not args.no_hbm_probe and args.workload == "batch200":
         probe = hbm_probe(torch, dev)

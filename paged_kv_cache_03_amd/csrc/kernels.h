@@ -96,8 +96,14 @@ constexpr int kGroupMaxMembers = 16;
 constexpr int kGroupWaves = 4;             // waves (heads) per workgroup
 constexpr int kGroupTiles = 3;             // tiles in each wave's load ring
 constexpr int kMaxGroupPartBlocks = 64;    // longest partition, in positions (blocks)
-constexpr int kGroupPartBlocks = 32;       // partition length the launch plan asks for
-constexpr int kGroupGridTarget = 1024;     // workgroups launched at most (grid-stride loop)
+#ifndef PKV_GROUP_PART
+#define PKV_GROUP_PART 32
+#endif
+#ifndef PKV_GROUP_GRID
+#define PKV_GROUP_GRID 1024
+#endif
+constexpr int kGroupPartBlocks = PKV_GROUP_PART;   // partition length the launch plan asks for
+constexpr int kGroupGridTarget = PKV_GROUP_GRID;   // workgroups launched at most (grid-stride loop)
 constexpr int kGroupMaxLdsBytes = 48 * 1024;
 
 struct GroupArgs {
