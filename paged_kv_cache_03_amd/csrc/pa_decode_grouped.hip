@@ -239,9 +239,11 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
     }
     __syncthreads();
 
-    // (cnt > 0 for every partition: (parts - 1) * plen < npos.  An empty
-    // item would still write empty partials: m = -inf, l = 0, acc = 0.)
-    if (h < a.H) {
+    // cnt > 0 for every partition ((parts - 1) * plen < npos); an empty item
+    // would still write empty partials (m = -inf, l = 0, acc = 0), in the
+    // branch after this one.  Entering the ring only with cnt > 0 keeps the
+    // compiled loop in the shape the load counters need.
+    if (h < a.H && cnt > 0) {
       // queries as the B operand: lane l holds member l%16's dims 32i + 8*(l/16) .. +7
       const rsrc_t qr = make_rsrc(a.q, (uint32_t)((size_t)a.B * a.H * D * 2));
       const uint32_t qoff = qc < gs.n
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
       const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
       const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
       auto fetch = [&](GTile<D>& t, int jpos) {
-        const int jj = max(0, min(jpos, cnt - 1));
+        const int jj = min(jpos, cnt - 1);
         const uint32_t bytes = jpos < cnt ? kTile : 0u;
         const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_id[jj]) * block_stride;
         const rsrc_t kr = make_rsrc(kbase + o, bytes);
@@ -354,6 +356,15 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
 #pragma unroll
         for (int s = 0; s < kS; ++s) dst[4 * s + tg] = acc[s];
       }
+    } else if (h < a.H && qc < gs.n) {
+      const size_t piece = ((size_t)(s_part[g] + part) * a.group_size + qc) * a.H + h;
+      if (tg == 0) {
+        a.ws_ml[piece * 2] = kNegInf;
+        a.ws_ml[piece * 2 + 1] = 0.0f;
+      }
+      f4v* dst = reinterpret_cast<f4v*>(a.ws_acc + piece * D);
+#pragma unroll
+      for (int s = 0; s < kS; ++s) dst[4 * s + tg] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     }
     __syncthreads();                   // LDS staging is reused by the next item
   }

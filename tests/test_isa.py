@@ -112,3 +112,34 @@ def test_no_spills_and_register_budget(flat_asm, part_asm):
     # partitioned one (<= 168)
     assert meta(flat_asm, "pa_decode_flat_kernelILi128E", "vgpr_count") <= 256
     assert meta(part_asm, "pa_decode_part_kernelILi128E", "vgpr_count") <= 168
+
+
+@pytest.fixture(scope="module")
+def grouped_asm(tmp_path_factory):
+    return device_asm("pa_decode_grouped.hip", tmp_path_factory.mktemp("isa"))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("policy", [2, 0])
+def test_grouped_ring_keeps_a_tile_in_flight(grouped_asm, D, policy):
+    """The grouped decode's tile loop (the one issuing the MFMAs) never
+    drains its loads, and no wait in it leaves less than one tile (2*D/32
+    loads) in flight; both products run on the matrix cores."""
+    body = kernel_body(grouped_asm, f"pa_decode_grouped_kernelILi{D}ELi{policy}E")
+    rings = [t for t in tile_loops(body).values() if "v_mfma" in t]
+    assert len(rings) == 1, "expected one MFMA tile loop"
+    ring = rings[0]
+    assert "vmcnt(0)" not in ring
+    waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", ring)]
+    assert waits and min(waits) >= 2 * (D // 32)
+    assert "v_mfma_f32_16x16x32_f16" in ring and "v_mfma_f32_16x16x16_f16" in ring
+    nt = re.search(r"buffer_load_dwordx4 .* offen( offset:\d+)? nt", ring)
+    assert bool(nt) == (policy == 2)
+
+
+def test_grouped_no_spills_and_register_budget(grouped_asm):
+    for D in (128, 64):
+        name = f"pa_decode_grouped_kernelILi{D}E"
+        assert meta(grouped_asm, name, "vgpr_spill_count") == 0
+        assert meta(grouped_asm, name, "private_segment_fixed_size") == 0
+        assert meta(grouped_asm, name, "vgpr_count") <= 256     # two waves per SIMD
