@@ -363,3 +363,91 @@ def test_grouped_contract_edges():
     offs = np.array([0, 3, 2, B - 1], dtype=np.int32)
     got = grouped_decode_ref(q, kp, vp, tables, lens, offs, [2, 2, 2], scale)
     assert np.array_equal(got[:3], plain[:3]) and not got[B - 1].any()
+
+
+# ------------------------------------------------------------------- prefill
+
+def _prefill_case(rng, H, D, lens, nq):
+    q_, kp, vp, tables, lens = _rand_case(rng, len(lens), H, D, lens)
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = rng.standard_normal((int(qs[-1]), H, D)).astype(np.float16)
+    return q, kp, vp, tables, lens, qs
+
+
+def test_prefill_matches_torch_sdpa_causal_float64():
+    """Every sequence's query rows against torch's float64 attention with an
+    explicit mask: row i (position ctx - n + i) sees keys 0 .. that position."""
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(31)
+    H, D = 3, 64
+    lens, nq = [37, 16, 70, 5], [37, 3, 20, 5]
+    q, kp, vp, tables, lens, qs = _prefill_case(rng, H, D, lens, nq)
+    scale = 0.125
+    out = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
+    for b in range(len(lens)):
+        n, ctx = nq[b], int(lens[b])
+        K = torch.from_numpy(gather_ref(kp, tables[b], ctx, H, D)).permute(1, 0, 2)
+        V = torch.from_numpy(gather_ref(vp, tables[b], ctx, H, D)).permute(1, 0, 2)
+        Q = torch.from_numpy(q[qs[b]:qs[b + 1]].astype(np.float64)).permute(1, 0, 2)
+        pos = torch.arange(ctx - n, ctx)[:, None]
+        mask = torch.arange(ctx)[None, :] <= pos                  # [n][ctx]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask,
+                                                               scale=scale)
+        np.testing.assert_allclose(out[qs[b]:qs[b + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_prefill_brute_force_tiny():
+    """Pure-Python loops over the pool at the documented element positions."""
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(32)
+    H, D = 2, 16
+    lens, nq = [19, 7], [4, 7]
+    q, kp, vp, tables, lens, qs = _prefill_case(rng, H, D, lens, nq)
+    scale = 0.25
+    out = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
+    kf, vf = kp.reshape(-1), vp.reshape(-1)
+    for b in range(2):
+        ctx, n = int(lens[b]), nq[b]
+        for i in range(n):
+            p = ctx - n + i
+            for h in range(H):
+                at = lambda t, d: pool_element_index(int(tables[b][t // 16]), h, t % 16, d, H, D)
+                s = [scale * math.fsum(float(q[qs[b] + i, h, d]) * float(kf[at(t, d)])
+                                       for d in range(D)) for t in range(p + 1)]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                den = math.fsum(w)
+                for d in range(D):
+                    num = math.fsum(w[t] * float(vf[at(t, d)]) for t in range(p + 1))
+                    assert abs(out[qs[b] + i, h, d] - num / den) <= 1e-12
+
+
+def test_prefill_position_zero_and_too_many_queries():
+    """The query at position 0 sees only its own token: the output is that
+    token's value exactly.  Rows past the context's start are zero."""
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(33)
+    H, D = 2, 64
+    q, kp, vp, tables, lens, qs = _prefill_case(rng, H, D, [9], [12])
+    out = paged_prefill_ref(q, kp, vp, tables, lens, qs, 0.125)
+    assert not out[:3].any()                                   # positions -3, -2, -1
+    v0 = gather_ref(vp, tables[0], 1, H, D)[0]
+    assert np.array_equal(out[3], v0.astype(np.float64))
+
+
+def test_prefill_chunks_agree_with_one_pass():
+    """Causal attention of a token depends on its prefix only: a prompt
+    processed in one call or in two chunks (the second over a longer cached
+    context) gives the same rows bit for bit; and the last row of each chunk
+    is the decode of the sequence at that length."""
+    from oracle import paged_prefill_ref
+    rng = np.random.default_rng(34)
+    H, D = 2, 64
+    q, kp, vp, tables, lens, qs = _prefill_case(rng, H, D, [53], [53])
+    whole = paged_prefill_ref(q, kp, vp, tables, lens, qs, 0.125)
+    first = paged_prefill_ref(q[:20], kp, vp, tables, np.array([20]), [0, 20], 0.125)
+    second = paged_prefill_ref(q[20:], kp, vp, tables, lens, [0, 33], 0.125)
+    assert np.array_equal(whole, np.concatenate([first, second]))
+    dec = paged_decode_ref(q[19:20], kp, vp, tables, np.array([20]), 0.125)
+    assert np.array_equal(first[19], dec[0])

@@ -46,6 +46,7 @@ class Case:
     slot_mapping: Optional[np.ndarray] = None  # int32 [T]
     cow_pairs: Optional[np.ndarray] = None     # int32 [n][2] (src, dst)
     shared_tables: Optional[np.ndarray] = None  # tables before copy-on-write
+    query_start: Optional[np.ndarray] = None    # int32 [B+1], prefill: rows of q per sequence
     num_layers: int = 1
     meta: dict = field(default_factory=dict)
 
@@ -274,6 +275,46 @@ def full_step(batch=200, layers=32, context=MAX_SEQ, seed=4, heads=32, head_dim=
                 k_new=k_new, v_new=v_new, slot_mapping=slots, cow_pairs=pairs,
                 shared_tables=shared, num_layers=layers)
     case.meta.update(seed=seed, beams=beams)
+    return case
+
+
+def prefill(batch=200, seed=6, cached=0, chunk=None, heads=32, head_dim=128, fill=True):
+    """Prefill of one layer: every sequence processes ``n_b`` new tokens as
+    queries (a prompt: U[32, 256] tokens, or a fixed ``chunk``) after
+    ``cached`` tokens already in its pages, so its context is cached + n_b.
+
+    ``q`` is [sum n_b][H][D] with sequence b's rows at
+    query_start[b] .. query_start[b+1]-1; ``k_new``/``v_new`` hold the new
+    tokens' keys and values with their ``slot_mapping`` (appended before the
+    attention); the pools (blocks needed plus 10%, shuffled) hold the cached
+    tokens."""
+    rng = np.random.default_rng(seed)
+    if chunk is None:
+        n = rng.integers(32, 256, size=batch, endpoint=True).astype(np.int32)
+    else:
+        n = np.full(batch, chunk, dtype=np.int32)
+    lens = (cached + n).astype(np.int32)
+    nblk = [_blocks(x) for x in lens]
+    need = int(sum(nblk))
+    num_blocks = -(-need * 11 // 10)
+    free = rng.permutation(num_blocks).astype(np.int32)
+    tables, _ = _tables(nblk, free, max(nblk))
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    T = int(qs[-1])
+    q = normal_fp16(rng, (T, heads, head_dim))
+    name = f"prefill_b{batch}" + (f"_c{cached}+{chunk}" if chunk is not None else "_prompt")
+    case = Case(name, heads, head_dim, num_blocks, lens, tables, q, _scale(head_dim),
+                query_start=qs)
+    case.meta.update(seed=seed, cached=cached, chunk=chunk)
+    if fill:
+        case.k_pool = normal_fp16(rng, pool_shape(num_blocks, heads, head_dim))
+        case.v_pool = normal_fp16(rng, pool_shape(num_blocks, heads, head_dim))
+    else:
+        rng = np.random.default_rng([seed, 1])
+    case.k_new = normal_fp16(rng, (T, heads, head_dim))
+    case.v_new = normal_fp16(rng, (T, heads, head_dim))
+    case.slot_mapping = np.array([_slot(tables[b], p) for b in range(batch)
+                                  for p in range(cached, int(lens[b]))], dtype=np.int32)
     return case
 
 
