@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = default)")
     ap.add_argument("--workload", default="batch200",
-                    choices=["batch200", "batch10", "shared_prefix", "full_step", "beam_step"],
+                    choices=["batch200", "batch10", "shared_prefix", "full_step", "beam_step",
+                             "prefill_prompt", "prefill_chunked"],
                     help="batch200 (default): the headline one-layer batch of 200")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0,
@@ -385,6 +386,57 @@ def setup_full_step(torch, dev, wl, args, beams):
                        "beams": beams, "seed": 4})
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+
+
+def setup_prefill(torch, dev, wl, args, chunked):
+    """One layer of prefill: per step the new tokens' keys and values are
+    appended through their slots, then every new token attends causally over
+    its sequence (pa_prefill).  Prompts: 200 sequences of U[32, 256] tokens;
+    chunked: 32 sequences, a 512-token chunk over 1536 cached tokens."""
+    from paged_kv_cache_03_amd import kv_append, pa_prefill
+    import numpy as np
+    case = wl.prefill(32, seed=7, cached=1536, chunk=512, fill=False) if chunked else \
+        wl.prefill(fill=False)
+    H, D = case.num_heads, case.head_dim
+    kp = wl.device_pool(torch, case, 0, 0, dev)
+    vp = wl.device_pool(torch, case, 0, 1, dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    q, tables, lens, qs = t(case.q), t(case.block_tables), t(case.context_lens), t(case.query_start)
+    kn, vn, slots = t(case.k_new), t(case.v_new), t(case.slot_mapping)
+    out = torch.empty_like(q)
+    max_ctx = case.max_context
+
+    def step(events):
+        kv_append(kn, vn, slots, kp, vp)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+        pa_prefill(q, kp, vp, tables, lens, qs, case.scale, out, max_context_len=max_ctx)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+
+    n = np.diff(case.query_start).astype(np.int64)
+    ctx = case.context_lens.astype(np.int64)
+    # causal (query, key) pairs: a chunk of n over c cached tokens sees c*n + n(n+1)/2
+    pairs = int(((ctx - n) * n + n * (n + 1) // 2).sum())
+    flops = 4 * H * D * pairs                          # q.k and p.v, 2 flops per multiply-add
+    kv_bytes = int(ctx.sum()) * H * D * 2 * 2          # every cached token's K and V once
+    io_bytes = int(n.sum()) * H * D * 2 * 2            # q read, out written
+    rows = int(n.sum())
+    return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=case.batch, kv_bytes=kv_bytes,
+               algo_bytes=kv_bytes + io_bytes, strategy="prefill", part=0,
+               prefill={"rows": rows, "flops": flops, "pairs": pairs},
+               extra={"query_rows": rows, "causal_pairs": pairs},
+               config={"workload": ("one layer, 32 sequences x (1536 cached + 512-token chunk)"
+                                    if chunked else "one layer, 200 prompts of U[32,256] tokens")
+                                   + ", 32 heads x 128 dims fp16; per step kv_append of the new "
+                                   "tokens + causal pa_prefill",
+                       "batch": case.batch, "heads": H, "head_dim": D, "block_tokens": 16,
+                       "query_rows": rows, "context_tokens": case.kv_tokens(),
+                       "max_context": max_ctx, "num_blocks": case.num_blocks,
+                       "seed": case.meta["seed"]})
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -414,6 +466,8 @@ def main():
         run = setup_batch(torch, dev, wl, args, 10, 1)
     elif args.workload == "shared_prefix":
         run = setup_shared_prefix(torch, dev, wl, args)
+    elif args.workload.startswith("prefill"):
+        run = setup_prefill(torch, dev, wl, args, args.workload == "prefill_chunked")
     else:
         run = setup_full_step(torch, dev, wl, args, 4 if args.workload == "beam_step" else 1)
     log(f"workload {args.workload}: {run.config}")
@@ -471,6 +525,27 @@ def main():
         },
     }
     result.update(run.extra)
+    pf = getattr(run, "prefill", None)
+    if pf is not None:
+        # prefill: the bound is whichever of HBM bytes and matrix flops takes longer
+        tflops = pf["flops"] / dec_avg_s / 1e12
+        t_hbm = run.algo_bytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = pf["flops"] / (MFMA_F16_PEAK_TFLOPS * 1e12)
+        result["metric"] = "pa_prefill tokens/s, TFLOP/s and GB/s (one layer)"
+        result["value"] = round(pf["rows"] / (ms_per_step / 1e3), 1)
+        result["unit"] = "tokens/s"
+        result["pa_prefill_us"] = result.pop("pa_decode_us")
+        result["pa_prefill_tflops"] = round(tflops, 2)
+        result["pa_prefill_gbs"] = round(achieved, 2)
+        for k in ("pa_decode_kv_gbs", "pa_decode_pct_hbm_peak", "pct_hbm_peak"):
+            result.pop(k, None)
+        if t_mfma >= t_hbm:
+            result["roofline"].update(kernel="pa_prefill", bound="mfma", unit="TFLOP/s",
+                                      achieved=round(tflops, 2), peak=MFMA_F16_PEAK_TFLOPS,
+                                      frac=round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                                      flops_per_launch=pf["flops"])
+        else:
+            result["roofline"].update(kernel="pa_prefill")
     if "unique_kv_bytes" in run.extra:      # per decode call: each distinct block once
         result["pa_decode_unique_kv_gbs"] = round(run.extra["unique_kv_bytes"] / dec_avg_s / 1e9, 2)
 

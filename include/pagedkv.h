@@ -238,6 +238,38 @@ size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,
                                             int32_t group_size);
 
 /*
+ * Paged prefill ("PagedAttention", e-fortepiano.pl, "Formulació
+ * matemàtica": causal self-attention over the paged cache, block by block):
+ * the last n_b = query_start[b+1] - query_start[b] tokens of every sequence
+ * b (its prompt, or a chunk of it, already written to its pages, e.g. with
+ * pkv_kv_append) are queries.  Query row r = query_start[b] + i sits at
+ * position p = context_lens[b] - n_b + i and
+ *
+ *   out[r][h] = sum_{t <= p} softmax_t(scale * q[r][h] . K_t) * V_t,
+ *
+ * with K_t / V_t read through block_tables[b] as for pkv_pa_decode (fp32
+ * arithmetic on the matrix cores, probabilities rounded to fp16 before the
+ * value product, fp16 output with round to nearest even).  Rows at a
+ * negative position (n_b > context_lens[b]) are zero rows.
+ *
+ * device: q and out [num_query_rows][H][D] fp16 (16-byte aligned), k_pool,
+ *         v_pool, block_tables, context_lens, query_start (B + 1 entries,
+ *         non-decreasing, query_start[B] <= num_query_rows; rows outside
+ *         [0, num_query_rows) are skipped).
+ * host:   sizes, scale, max_context_len (>= every context_lens[b]; contexts
+ *         are clamped to it), block_size 16, flags 0 (reserved).  The block
+ *         ids of one sequence are staged in LDS: (B + 1 + max_context_len /
+ *         16) * 4 bytes must not exceed 32 KiB.  No workspace.
+ */
+int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len,
+                   const int32_t* query_start, int32_t num_query_rows,
+                   int32_t B, int32_t H, int32_t D, int32_t block_size,
+                   int32_t num_blocks, float scale, void* out, uint32_t flags,
+                   void* stream);
+
+/*
  * Measurement aids, not part of the decode path.  Each reads `bytes` (a
  * multiple of 16) of device memory `buf` with 16-byte non-temporal loads
  * from `workgroups` workgroups of 256 threads, asynchronously on `stream`,

@@ -14,4 +14,4 @@ from .blocks import (PAGE_TOKENS, PagedRequest, PagePool, PoolExhausted,  # noqa
                      decode_groups, device_arrays, kv_bytes_per_token, tables_share_blocks)
 from .ops import (cow_copy_blocks, default_partition, kv_append, pa_decode,  # noqa: F401
                   pa_decode_grouped, pa_decode_grouped_workspace_size, pa_decode_workspace_size,
-                  pool_shape)
+                  pa_prefill, pool_shape)

@@ -324,13 +324,61 @@ int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len,
+                   const int32_t* query_start, int32_t num_query_rows, int32_t B, int32_t H,
+                   int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                   uint32_t flags, void* stream) {
+  if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
+  if (flags != 0) return PKV_ERR_BAD_SHAPE;
+  if (!decode_shape_ok(B, H, D, max_context_len) || num_query_rows < 0 ||
+      (long long)num_query_rows * H * D * 2 >= (1LL << 32))
+    return PKV_ERR_BAD_SHAPE;
+  if (B == 0 || num_query_rows == 0) return PKV_OK;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      (long long)max_blocks_per_seq * kBlockTokens < max_context_len)
+    return PKV_ERR_BAD_SHAPE;
+  const int32_t blocks_used = ceil_div(max_context_len, kBlockTokens);
+  if (pkv::prefill_lds_bytes(B, blocks_used) > (size_t)pkv::kPrefillMaxLdsBytes)
+    return PKV_ERR_BAD_SHAPE;
+  const int32_t head_groups = (H + pkv::kPrefillWaves - 1) / pkv::kPrefillWaves;
+  // tiles: sum over sequences of ceil(n_b / 16) <= num_query_rows / 16 + B
+  const long long grid = ((long long)ceil_div(num_query_rows, 16) + B) * head_groups;
+  if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out)
+    return PKV_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PKV_ERR_MISALIGNED;
+  pkv::PrefillArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = static_cast<_Float16*>(out);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.B = B;
+  a.H = H;
+  a.num_rows = num_query_rows;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_limit = max_context_len;
+  a.num_blocks = num_blocks;
+  a.head_groups = head_groups;
+  const hipError_t e = pkv::launch_pa_prefill(a, D, (int)grid, blocks_used,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pkv_kv_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,
                   void* k_pool, void* v_pool, int32_t num_blocks, int32_t H, int32_t D,
                   int32_t block_size, void* stream) {
   if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
   if (T < 0 || H <= 0 || !head_dim_ok(D) || num_blocks <= 0) return PKV_ERR_BAD_SHAPE;
   if (T == 0) return PKV_OK;
-  if ((long long)T * H * (D / 8) >= (1LL << 31) * 256LL) return PKV_ERR_BAD_SHAPE;
+  if (((long long)T + 15) / 16 * 16 * H * (D / 8) >= (1LL << 31) * 256LL) return PKV_ERR_BAD_SHAPE;
   if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_NULL_PTR;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(slot_mapping, 4))

@@ -4,9 +4,15 @@
 // Append ("Atención paginada en modelos de lenguaje grandes (LLM)",
 // 7minutos.es, PagePool / PagedRequest part): a generated token is stored in
 // the page its block table names.  One thread moves one 16-byte group (8
-// dims of one head of one token) of K and the same group of V: the source
-// rows are read fully coalesced, the destination groups sit 256 bytes apart
-// inside their tile (layout [block][H][D/8][16][8]).
+// dims of one head of one token) of K and the same group of V, with one of
+// two lane mappings (layout [block][H][D/8][16][8]):
+//  * a few tokens, each in its own block (a decode step): consecutive
+//    lanes take consecutive groups of one token, so the source rows are
+//    read fully coalesced (the destinations sit 256 bytes apart);
+//  * many tokens (a prompt, a chunk): within a (head, group), 16 consecutive
+//    tokens go to 16 consecutive lanes, so tokens at consecutive positions
+//    of one block fill a whole 256-byte row of the tile per 16 lanes, and a
+//    wave still reads 64 contiguous bytes of each source row.
 //
 // Copy-on-write (same page, prefix-sharing part; "PagedAttention",
 // e-fortepiano.pl, "Descripció"): a shared page that must change is first
@@ -23,15 +29,31 @@ namespace {
 
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 constexpr int kBlockTokens = 16;
+// From this many tokens on, an append is taken to be runs of consecutive
+// positions (a prompt or chunk) and uses the token-per-lane mapping.
+constexpr int kAppendRunsFrom = 1024;
 
+template <bool kRuns>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int groups = a.D / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)a.T * a.H * groups;
-  if (idx >= total) return;
-  const int c = (int)(idx % groups);
-  const int h = (int)((idx / groups) % a.H);
-  const int t = (int)(idx / ((long long)groups * a.H));
+  int t, h, c;
+  if (kRuns) {
+    const long long runs = (a.T + kBlockTokens - 1) / kBlockTokens;
+    if (idx >= runs * kBlockTokens * a.H * groups) return;
+    const int tin = (int)(idx % kBlockTokens);
+    const long long rest = idx / kBlockTokens;
+    c = (int)(rest % groups);
+    h = (int)((rest / groups) % a.H);
+    const long long t64 = (rest / ((long long)groups * a.H)) * kBlockTokens + tin;
+    if (t64 >= a.T) return;
+    t = (int)t64;
+  } else {
+    if (idx >= (long long)a.T * a.H * groups) return;
+    c = (int)(idx % groups);
+    h = (int)((idx / groups) % a.H);
+    t = (int)(idx / ((long long)groups * a.H));
+  }
   const int slot = a.slots[t];
   if (slot < 0) return;
   const int blk = slot / kBlockTokens;
@@ -72,10 +94,15 @@ __global__ __launch_bounds__(256) void cow_copy_kernel(CowArgs a) {
 }  // namespace
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
-  const long long total = (long long)a.T * a.H * (a.D / 8);
+  const bool runs = a.T >= kAppendRunsFrom;
+  const long long tokens = runs ? (a.T + kBlockTokens - 1) / kBlockTokens * kBlockTokens : a.T;
+  const long long total = tokens * a.H * (a.D / 8);
   const int threads = 256;
   const long long grid = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(threads), 0, stream, a);
+  if (runs)
+    hipLaunchKernelGGL(kv_append_kernel<true>, dim3((unsigned)grid), dim3(threads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<false>, dim3((unsigned)grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -130,6 +130,28 @@ struct GroupArgs {
   bool keep_cached;
 };
 
+// Prefill (pa_prefill.hip): one workgroup per (16-query tile, head group).
+constexpr int kPrefillWaves = 4;           // waves (heads) per workgroup
+constexpr int kPrefillTiles = 3;           // tiles in each wave's load ring
+constexpr int kPrefillMaxLdsBytes = 32 * 1024;
+
+struct PrefillArgs {
+  const _Float16* q;            // [num_rows][H][D]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;   // [B + 1]: sequence b's rows are [qs[b], qs[b+1])
+  _Float16* out;                // [num_rows][H][D]
+  float scale_log2;
+  int B, H;
+  int num_rows;
+  int max_blocks;
+  int ctx_limit;
+  int num_blocks;
+  int head_groups;              // ceil(H / kPrefillWaves)
+};
+
 struct AppendArgs {
   const void* k;
   const void* v;
@@ -162,6 +184,9 @@ hipError_t launch_hbm_gather_probe(const void* buf, const int32_t* order, long l
                                    int log_kib, uint32_t* sink, int grid, hipStream_t stream);
 hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, int grid, hipStream_t stream);
 size_t grouped_lds_bytes(int G);
+hipError_t launch_pa_prefill(const PrefillArgs& a, int D, int grid, int max_blocks_used,
+                             hipStream_t stream);
+size_t prefill_lds_bytes(int B, int max_blocks_used);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_cow_copy(const CowArgs& a, hipStream_t stream);
 

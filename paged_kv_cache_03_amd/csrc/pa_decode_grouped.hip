@@ -16,19 +16,8 @@
 // items in a grid-stride loop, one wave per head, and stages the item's
 // block ids and masks in LDS.
 //
-// Per 16-token tile the arithmetic is two small dense contractions, on the
-// matrix cores:
-//  * scores S^T (16 tokens x 16 queries) = K (16 x D) . Q^T (D x 16) with
-//    v_mfma_f32_16x16x32_f16: the K tile as loaded (lane l: token l%16,
-//    dims 32i + 8*(l/16) .. +7) is already the A operand of the i-th MFMA,
-//    the queries are the B operand (lane l: query l%16, same dims);
-//  * online softmax per query column (the four lanes l%16 + 16*r hold one
-//    query's 16 scores, combined with permlane swaps), weights rounded to
-//    fp16 once and the running sum taken over the rounded weights;
-//  * O^T (D x 16 queries) += V^T (D x 16 tokens) . P^T (16 tokens x 16
-//    queries) with v_mfma_f32_16x16x16_f16: P^T is the score accumulator's
-//    own layout, V^T is read back transposed from the wave's LDS copy of the
-//    V tile.
+// Per 16-token tile the arithmetic is two small dense contractions on the
+// matrix cores, one MFMA column per member (pa_mfma.h).
 // Each item ends with one partial result (m, l, acc[D]) per member; a merge
 // kernel combines a member's partials in partition order.
 
@@ -37,26 +26,16 @@
 
 #include "kernels.h"
 #include "pa_common.h"
+#include "pa_mfma.h"
 
 namespace pkv {
 namespace {
 
 using namespace dev;
 
-typedef _Float16 h4v __attribute__((ext_vector_type(4)));
-typedef float f4v __attribute__((ext_vector_type(4)));
-
 constexpr int kInfoShared = 0;        // member field of a shared position
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
-
-// Maximum over the four rows of 16 lanes (same pattern as cross_row_sum).
-__device__ __forceinline__ float cross_row_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
-  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
-  return fmaxf(as_f32(b[0]), as_f32(b[1]));
-}
 
 // Group g's members [lo, lo + n) and its position count; every bound the
 // contract states is applied here, so device data cannot push an index out
@@ -131,12 +110,6 @@ __device__ __forceinline__ int group_of(const int* s_part, int G, int gp) {
   }
   return lo;
 }
-
-template <int D>
-struct GTile {
-  u4v k[D / 32];
-  u4v v[D / 32];
-};
 
 template <int D, int kPolicy>
 __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(GroupArgs a) {
@@ -260,18 +233,12 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
 
       const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
       const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
-      auto fetch = [&](GTile<D>& t, int jpos) {
+      auto fetch = [&](MTile<D>& t, int jpos) {
         const int jj = min(jpos, cnt - 1);
         const uint32_t bytes = jpos < cnt ? kTile : 0u;
         const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_id[jj]) * block_stride;
-        const rsrc_t kr = make_rsrc(kbase + o, bytes);
-        const rsrc_t vr = make_rsrc(vbase + o, bytes);
-#pragma unroll
-        for (int i = 0; i < kK; ++i)
-          t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * 1024, 0, kPolicy);
-#pragma unroll
-        for (int i = 0; i < kK; ++i)
-          t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * 1024, 0, kPolicy);
+        mfma_fetch<D, kPolicy>(t, make_rsrc(kbase + o, bytes), make_rsrc(vbase + o, bytes),
+                               lane_off);
       };
 
       float m = kNegInf, l = 0.0f;     // for query qc; l over this lane's tokens only
@@ -283,58 +250,16 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
       // score is -inf, alpha = 1 and every weight and value 0, so it changes
       // nothing; that keeps the ring loop free of exits in its body (an exit
       // there lets the compiler sink the prefetches down to their use).
-      auto step = [&](const GTile<D>& t, int jpos) {
+      auto step = [&](const MTile<D>& t, int jpos) {
         const int info = jpos < cnt ? __builtin_amdgcn_readfirstlane(s_info[jpos]) : 0;
         const int member = info & 0xff;
         const int valid = info >> 8;
-        f4v sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < kK; ++i)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(t.k[i]), qb[i], sc, 0, 0, 0);
         const bool qok = qc < gs.n && (member == kInfoShared || qc == member - 1);
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[r] = (qok && 4 * tg + r < valid) ? sc[r] * a.scale_log2 : kNegInf;
-          mx = fmaxf(mx, sc[r]);
-        }
-        const float mnew = fmaxf(m, cross_row_max(mx));
-        const float mref = mnew == kNegInf ? 0.0f : mnew;
-        const float alpha = exp2f(m - mref);
-        h4v pb;
-        float psum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb[r] = (_Float16)exp2f(sc[r] - mref);
-          psum += (float)pb[r];
-        }
-        l = fmaf(l, alpha, psum);
-        m = mnew;
-        // V^T through LDS; slots past `valid` are zeroed first (they may hold
-        // anything, NaN included, and weight 0 * NaN would still be NaN)
-        const bool tok_ok = qc < valid;          // this lane's loaded token is l % 16
-#pragma unroll
-        for (int i = 0; i < kK; ++i) {
-          u4v w = t.v[i];
-          w.x = tok_ok ? w.x : 0u;
-          w.y = tok_ok ? w.y : 0u;
-          w.z = tok_ok ? w.z : 0u;
-          w.w = tok_ok ? w.w : 0u;
-          sv[i * kWave + lane] = w;
-        }
-#pragma unroll
-        for (int s = 0; s < kS; ++s) {
-          const int d = 16 * s + qc;
-          const int base = ((d >> 3) * kBlockTokens + 4 * tg) * 8 + (d & 7);
-          h4v va;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) va[e] = svh[base + e * 8];
-          acc[s] = acc[s] * alpha;
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[s], 0, 0, 0);
-        }
+        mfma_update<D>(t, qb, a.scale_log2, valid, [&](int tok) { return qok && tok < valid; },
+                       m, l, acc, sv, svh, lane);
       };
 
-      GTile<D> t[kGroupTiles];
+      MTile<D> t[kGroupTiles];
 #pragma unroll
       for (int k = 0; k + 1 < kGroupTiles; ++k) fetch(t[k], k);
       for (int jpos = 0; jpos < cnt; jpos += kGroupTiles) {

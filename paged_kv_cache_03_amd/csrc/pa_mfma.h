@@ -1,0 +1,116 @@
+// Multi-query attention over one 16-token (block, head) tile on the gfx950
+// matrix cores (internal), shared by the grouped decode and the prefill.
+//
+// A wave serves up to 16 query rows at once, one per MFMA column: lane l
+// belongs to query column l%16 and to quarter tg = l/16.
+//  * scores S^T (16 tokens x 16 queries) = K (16 x D) . Q^T (D x 16), one
+//    v_mfma_f32_16x16x32_f16 per 32 dims.  The K tile as loaded (lane l:
+//    token l%16, dims 32i + 8*tg .. +7) is exactly the A operand of the i-th
+//    MFMA; the queries are the B operand (lane l: query l%16, same dims).
+//    The result's lane l holds tokens 4*tg + r (r < 4) of query l%16.
+//  * online softmax per query column: the four lanes l%16 + 16*tg hold one
+//    query's 16 scores and are combined with permlane swaps; the weights are
+//    rounded to fp16 once and the running sum uses the rounded weights.
+//  * O^T (D x 16 queries) += V^T (D x 16 tokens) . P^T (16 tokens x 16
+//    queries), one v_mfma_f32_16x16x16_f16 per 16 output dims.  P^T is the
+//    score result's own layout; V^T is read back transposed from the wave's
+//    LDS copy of the V tile.  acc[s] lane l: dims 16s + 4*tg + r of query
+//    l%16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_common.h"
+
+namespace pkv {
+namespace dev {
+
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Maximum over the four rows of 16 lanes (same pattern as cross_row_sum).
+__device__ __forceinline__ float cross_row_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(as_f32(b[0]), as_f32(b[1]));
+}
+
+template <int D>
+struct MTile {
+  u4v k[D / 32];
+  u4v v[D / 32];
+};
+
+template <int D, int kPolicy>
+__device__ __forceinline__ void mfma_fetch(MTile<D>& t, rsrc_t kr, rsrc_t vr, uint32_t lane_off) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * 1024, 0, kPolicy);
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * 1024, 0, kPolicy);
+}
+
+// One tile.  live(tok) says whether token tok (0..15 of the tile) is
+// attended by this lane's query column; tokens at or past `valid` hold no
+// data and must not be live (their V rows are zeroed: they may hold
+// anything, NaN included, and weight 0 * NaN would still be NaN).
+// sv / svh: the wave's own LDS area of D * 16 fp16 (the wave's LDS
+// operations run in order, so no barrier is needed).
+template <int D, typename Live>
+__device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D / 32],
+                                            float scale_log2, int valid, Live live, float& m,
+                                            float& l, f4v (&acc)[D / 16], u4v* sv,
+                                            const _Float16* svh, int lane) {
+  constexpr int kK = D / 32;
+  constexpr int kS = D / 16;
+  const int qc = lane % 16;
+  const int tg = lane / 16;
+  f4v sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kK; ++i)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(t.k[i]), qb[i], sc, 0, 0, 0);
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = live(4 * tg + r) ? sc[r] * scale_log2 : kNegInf;
+    mx = fmaxf(mx, sc[r]);
+  }
+  const float mnew = fmaxf(m, cross_row_max(mx));
+  const float mref = mnew == kNegInf ? 0.0f : mnew;
+  const float alpha = exp2f(m - mref);
+  h4v pb;
+  float psum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pb[r] = (_Float16)exp2f(sc[r] - mref);
+    psum += (float)pb[r];
+  }
+  l = fmaf(l, alpha, psum);
+  m = mnew;
+  const bool tok_ok = qc < valid;      // this lane's loaded token is l % 16
+#pragma unroll
+  for (int i = 0; i < kK; ++i) {
+    u4v w = t.v[i];
+    w.x = tok_ok ? w.x : 0u;
+    w.y = tok_ok ? w.y : 0u;
+    w.z = tok_ok ? w.z : 0u;
+    w.w = tok_ok ? w.w : 0u;
+    sv[i * kWave + lane] = w;
+  }
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    const int d = 16 * s + qc;
+    const int base = ((d >> 3) * kBlockTokens + 4 * tg) * 8 + (d & 7);
+    h4v va;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) va[e] = svh[base + e * 8];
+    acc[s] = acc[s] * alpha;
+    acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[s], 0, 0, 0);
+  }
+}
+
+}  // namespace dev
+}  // namespace pkv

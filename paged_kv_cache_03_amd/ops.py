@@ -166,6 +166,42 @@ def pa_decode_grouped(q, k_pool, v_pool, block_tables, context_lens, group_offse
     return out
 
 
+def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, out=None, *,
+               max_context_len=None):
+    """Causal attention of each sequence's last n_b cached tokens (its rows
+    query_start[b] .. query_start[b+1]-1 of q, [T][H][D] fp16) over its paged
+    cache: row i of sequence b sits at position context_lens[b] - n_b + i.
+    ``query_start`` is an int32 device tensor of B+1 entries; the other
+    arguments are as for ``pa_decode``."""
+    lib = _lib.load_library()
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    T, H, D = q.shape
+    NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
+    if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
+        raise ValueError("k_pool and v_pool differ in size")
+    _need(block_tables, "block_tables", torch.int32, dev, ndim=2)
+    _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
+    _need(query_start, "query_start", torch.int32, dev, ndim=1)
+    B = context_lens.shape[0]
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables / query_start do not match context_lens")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, dev, ndim=3)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError("out must have the shape of q")
+    with torch.cuda.device(dev):
+        code = lib.pkv_pa_prefill(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), max_context_len, _ptr(query_start), T, B, H, D, BLOCK_TOKENS, NB,
+            float(scale), _ptr(out), 0, _stream_handle(dev))
+    _lib.check("pkv_pa_prefill", code)
+    return out
+
+
 def kv_append(k, v, slot_mapping, k_pool, v_pool):
     """Write row t of k / v ([T][H][D] fp16) into slot slot_mapping[t]
     (block slot//16, position slot%16) of one layer's pools; negative slots

@@ -235,3 +235,27 @@ def test_grouped_workspace_size():
                    ws(200, 32, 128, 2048, 150, 4)):
         assert bigger > base
     assert ws(200, 32, 64, 2048, 50, 4) < base
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    f = lib.pkv_pa_prefill
+
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, tables=A16, mb=128, lens=A16, max_ctx=2048, qs=A16, T=512,
+                 B=8, H=32, D=128, bs=16, NB=64, scale=0.1, out=A16, flags=0)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["tables"], a["mb"], a["lens"], a["max_ctx"], a["qs"],
+                 a["T"], a["B"], a["H"], a["D"], a["bs"], a["NB"], a["scale"], a["out"],
+                 a["flags"], None)
+
+    assert call(bs=8) == _lib.ERR_UNSUPPORTED
+    assert call(flags=1) == _lib.ERR_BAD_SHAPE
+    assert call(T=-1) == _lib.ERR_BAD_SHAPE
+    assert call(D=80) == _lib.ERR_BAD_SHAPE
+    assert call(mb=64) == _lib.ERR_BAD_SHAPE                 # table narrower than the context
+    assert call(B=9000) == _lib.ERR_BAD_SHAPE                # staging would not fit in LDS
+    assert call(T=0, q=None) == _lib.OK and call(B=0, q=None) == _lib.OK
+    assert call(qs=None) == _lib.ERR_NULL_PTR
+    assert call(out=None) == _lib.ERR_NULL_PTR
+    assert call(q=A4) == _lib.ERR_MISALIGNED
+    assert call(qs=A16 + 2) == _lib.ERR_MISALIGNED

@@ -143,3 +143,20 @@ def test_grouped_no_spills_and_register_budget(grouped_asm):
         assert meta(grouped_asm, name, "vgpr_spill_count") == 0
         assert meta(grouped_asm, name, "private_segment_fixed_size") == 0
         assert meta(grouped_asm, name, "vgpr_count") <= 256     # two waves per SIMD
+
+
+@pytest.fixture(scope="module")
+def prefill_asm(tmp_path_factory):
+    return device_asm("pa_prefill.hip", tmp_path_factory.mktemp("isa"))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D):
+    body = kernel_body(prefill_asm, f"pa_prefill_kernelILi{D}ELi0E")
+    rings = [t for t in tile_loops(body).values() if "v_mfma" in t]
+    assert len(rings) == 1, "expected one MFMA tile loop"
+    assert "vmcnt(0)" not in rings[0]
+    waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", rings[0])]
+    assert waits and min(waits) >= 2 * (D // 32)
+    assert meta(prefill_asm, f"pa_prefill_kernelILi{D}E", "vgpr_spill_count") == 0
+    assert meta(prefill_asm, f"pa_prefill_kernelILi{D}E", "vgpr_count") <= 256
