@@ -270,6 +270,83 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                    void* stream);
 
 /*
+ * Contiguous KV cache in virtual memory, physical memory on demand: the
+ * alternative to paging that "PagedAttention" (e-fortepiano.pl) describes in
+ * "Limitacions i alternatives" and "Atenció" (vAttention).  Each layer's K
+ * and V cache is one contiguous virtual buffer [max_batch][max_context][H][D]
+ * fp16 (request b owns rows b*max_context .. +max_context-1), reserved up
+ * front; physical memory is mapped into a request's part of every buffer,
+ * chunk_bytes at a time, as it grows.  Built on the HIP virtual memory API
+ * of the current device.  Calls are synchronous on the host and not
+ * thread-safe.
+ *
+ * pkv_vkv_create: max_context a multiple of 16; D 64 or 128; chunk_bytes a
+ *   multiple of the device's mapping granularity that divides
+ *   max_context*H*D*2.  Reserves 2*num_layers buffers; maps nothing.
+ * pkv_vkv_grow: maps chunks until request `seq` can hold `tokens` tokens
+ *   (rounded up to 16) in every layer.  Chunks of released requests are
+ *   reused before new physical memory is created.  Never shrinks.
+ * pkv_vkv_release: waits for the device, then unmaps all of `seq`'s chunks
+ *   (kept for reuse) and sets its readable tokens to 0.
+ * pkv_vkv_destroy: waits for the device, unmaps and frees everything.
+ * pkv_vkv_buffers: the K and V virtual buffers of `layer` (device
+ *   pointers; only rows below a request's readable tokens are mapped).
+ * pkv_vkv_capacity: device int32 [max_batch], each request's readable
+ *   tokens (its mapped rows, a multiple of 16, at most max_context); pass it
+ *   to pkv_contig_decode so that no unmapped row is ever read.
+ * pkv_vkv_append: asynchronously on `stream`, writes row t of k / v
+ *   ([T][H][D] fp16, device) as token positions[t] of request seq_ids[t]
+ *   in `layer` (device int32 arrays); rows outside a request's readable
+ *   tokens or with an invalid request are skipped.
+ * pkv_vkv_stats: physical bytes mapped (all buffers), bytes pooled for
+ *   reuse, bytes reserved, the chunk size, the granularity, map calls,
+ *   chunks created and host seconds spent mapping.
+ */
+typedef struct pkv_vkv pkv_vkv;
+
+typedef struct pkv_vkv_info {
+  uint64_t mapped_bytes;
+  uint64_t pooled_bytes;
+  uint64_t reserved_bytes;
+  uint64_t chunk_bytes;
+  uint64_t granularity;
+  uint64_t map_calls;
+  uint64_t chunks_created;
+  double map_seconds;
+} pkv_vkv_info;
+
+int pkv_vkv_create(int32_t max_batch, int32_t max_context, int32_t num_layers, int32_t H,
+                   int32_t D, size_t chunk_bytes, pkv_vkv** out);
+int pkv_vkv_destroy(pkv_vkv* vkv);
+int pkv_vkv_grow(pkv_vkv* vkv, int32_t seq, int32_t tokens);
+int pkv_vkv_release(pkv_vkv* vkv, int32_t seq);
+int pkv_vkv_buffers(const pkv_vkv* vkv, int32_t layer, void** k_buf, void** v_buf);
+const int32_t* pkv_vkv_capacity(const pkv_vkv* vkv);
+int pkv_vkv_append(const pkv_vkv* vkv, int32_t layer, const void* k, const void* v,
+                   const int32_t* seq_ids, const int32_t* positions, int32_t T, void* stream);
+int pkv_vkv_stats(const pkv_vkv* vkv, pkv_vkv_info* info);
+
+/*
+ * Decode over a contiguous KV cache ("PagedAttention", e-fortepiano.pl,
+ * "Atenció": the standard attention, unchanged, on contiguous K and V):
+ * out[b][h] as for pkv_pa_decode, with token t of sequence b read from row
+ * b*row_tokens + t of k_buf / v_buf ([rows][H][D] fp16, device).  The same
+ * flat-strategy kernel as pkv_pa_decode, addressing rows instead of table
+ * entries.  `capacity` (device int32 [B], may be NULL): tokens each
+ * sequence may read; contexts are clamped to it (pkv_vkv_capacity).
+ * row_tokens: a multiple of 16, >= max_context_len.  flags must be 0.  The
+ * workspace (256-byte aligned) is pkv_contig_decode_workspace_size bytes.
+ * Returns PKV_ERR_UNSUPPORTED for batches too large for the flat strategy.
+ */
+int pkv_contig_decode(const void* q, const void* k_buf, const void* v_buf, int32_t row_tokens,
+                      const int32_t* context_lens, const int32_t* capacity,
+                      int32_t max_context_len, int32_t B, int32_t H, int32_t D, float scale,
+                      void* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                      void* stream);
+size_t pkv_contig_decode_workspace_size(int32_t B, int32_t H, int32_t D,
+                                        int32_t max_context_len);
+
+/*
  * Measurement aids, not part of the decode path.  Each reads `bytes` (a
  * multiple of 16) of device memory `buf` with 16-byte non-temporal loads
  * from `workgroups` workgroups of 256 threads, asynchronously on `stream`,

@@ -35,3 +35,4 @@ from .paged_attention import (  # noqa: F401
 from .cache_ops import append_ref, cow_ref  # noqa: F401
 from .grouped import grouped_decode_ref, grouped_tables_ref  # noqa: F401
 from .prefill import paged_prefill_ref  # noqa: F401
+from .contiguous import contiguous_decode_ref  # noqa: F401

@@ -42,6 +42,17 @@ SIGNATURES = {
     "pkv_pa_decode_grouped_workspace_size": (_c.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_pa_prefill": (_c.c_int, [_vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32p, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _c.c_float, _vp, _c.c_uint32, _vp]),
+    "pkv_contig_decode": (_c.c_int, [_vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32,
+                                     _c.c_float, _vp, _vp, _c.c_size_t, _c.c_uint32, _vp]),
+    "pkv_contig_decode_workspace_size": (_c.c_size_t, [_i32, _i32, _i32, _i32]),
+    "pkv_vkv_create": (_c.c_int, [_i32, _i32, _i32, _i32, _i32, _c.c_size_t, _c.POINTER(_vp)]),
+    "pkv_vkv_destroy": (_c.c_int, [_vp]),
+    "pkv_vkv_grow": (_c.c_int, [_vp, _i32, _i32]),
+    "pkv_vkv_release": (_c.c_int, [_vp, _i32]),
+    "pkv_vkv_buffers": (_c.c_int, [_vp, _i32, _c.POINTER(_vp), _c.POINTER(_vp)]),
+    "pkv_vkv_capacity": (_vp, [_vp]),
+    "pkv_vkv_append": (_c.c_int, [_vp, _i32, _vp, _vp, _i32p, _i32p, _i32, _vp]),
+    "pkv_vkv_stats": (_c.c_int, [_vp, _vp]),
     "pkv_kv_append": (_c.c_int, [_vp, _vp, _i32p, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pkv_cow_copy_blocks": (_c.c_int, [_c.POINTER(_vp), _c.POINTER(_vp), _i32, _i32p, _i32, _i32,
                                        _c.c_int64, _vp]),
@@ -50,6 +61,14 @@ SIGNATURES = {
     "pkv_status_string": (_c.c_char_p, [_c.c_int]),
     "pkv_abi_version": (_i32, []),
 }
+
+
+class VkvInfo(_c.Structure):
+    """pkv_vkv_info of the C header."""
+    _fields_ = [("mapped_bytes", _c.c_uint64), ("pooled_bytes", _c.c_uint64),
+                ("reserved_bytes", _c.c_uint64), ("chunk_bytes", _c.c_uint64),
+                ("granularity", _c.c_uint64), ("map_calls", _c.c_uint64),
+                ("chunks_created", _c.c_uint64), ("map_seconds", _c.c_double)]
 
 
 class LibraryMissing(RuntimeError):

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedkv.so"
-SOURCES = ["api.hip", "pa_decode.hip", "pa_decode_flat.hip", "pa_decode_grouped.hip", "pa_prefill.hip", "cache_ops.hip", "probe.hip"]
+SOURCES = ["api.hip", "pa_decode.hip", "pa_decode_flat.hip", "pa_decode_grouped.hip", "pa_prefill.hip", "cache_ops.hip", "probe.hip", "vkv.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

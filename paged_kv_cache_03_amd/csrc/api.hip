@@ -219,6 +219,9 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
     a.nr = plan.nr;
     a.max_chunk = plan.max_chunk;
     a.keep_cached = keep_cached;
+    a.contig = false;
+    a.row_tokens = 0;
+    a.capacity = nullptr;
     e = pkv::launch_pa_decode_flat(a, D, fw * 64, static_cast<hipStream_t>(stream));
   } else {
     const long long grid = (long long)B * (H / wpg) * (plan.max_parts > 0 ? plan.max_parts : 1);
@@ -256,6 +259,61 @@ int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
   return pkv_pa_decode_ex(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                           max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
                           workspace_bytes, 0, 0u, stream);
+}
+
+size_t pkv_contig_decode_workspace_size(int32_t B, int32_t H, int32_t D,
+                                        int32_t max_context_len) {
+  if (!decode_shape_ok(B, H, D, max_context_len) || B == 0) return 0;
+  const Plan p = make_plan(B, H, D, max_context_len, 0);
+  return p.flat ? p.total : 0;
+}
+
+int pkv_contig_decode(const void* q, const void* k_buf, const void* v_buf, int32_t row_tokens,
+                      const int32_t* context_lens, const int32_t* capacity,
+                      int32_t max_context_len, int32_t B, int32_t H, int32_t D, float scale,
+                      void* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                      void* stream) {
+  if (flags != 0) return PKV_ERR_BAD_SHAPE;
+  if (!decode_shape_ok(B, H, D, max_context_len)) return PKV_ERR_BAD_SHAPE;
+  if (B == 0) return PKV_OK;
+  if (row_tokens <= 0 || row_tokens % kBlockTokens || row_tokens < max_context_len ||
+      (long long)B * (row_tokens / kBlockTokens) >= (1LL << 31) ||
+      (long long)H * D * 2 * kBlockTokens >= (1LL << 31))
+    return PKV_ERR_BAD_SHAPE;
+  const Plan plan = make_plan(B, H, D, max_context_len, 0);
+  if (!plan.flat) return PKV_ERR_UNSUPPORTED;
+  if (!q || !k_buf || !v_buf || !context_lens || !out || !workspace) return PKV_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(k_buf, 16) || !aligned(v_buf, 16) || !aligned(out, 16) ||
+      !aligned(context_lens, 4) || !aligned(capacity, 4) || !aligned(workspace, kWsAlign))
+    return PKV_ERR_MISALIGNED;
+  if (workspace_bytes < plan.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  const int fw = flat_waves_per_group(H);
+  pkv::FlatArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pool = k_buf;
+  a.v_pool = v_buf;
+  a.block_tables = nullptr;
+  a.context_lens = context_lens;
+  a.out = static_cast<_Float16*>(out);
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes);
+  a.ws_seq = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.seq_offset);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.B = B;
+  a.H = H;
+  a.max_blocks = row_tokens / kBlockTokens;
+  a.ctx_limit = max_context_len;
+  a.num_blocks = B * (row_tokens / kBlockTokens);
+  a.head_groups = H / fw;
+  a.waves_per_group = fw;
+  a.nr = plan.nr;
+  a.max_chunk = plan.max_chunk;
+  a.keep_cached = false;
+  a.contig = true;
+  a.row_tokens = row_tokens;
+  a.capacity = capacity;
+  const hipError_t e = pkv::launch_pa_decode_flat(a, D, fw * 64, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,

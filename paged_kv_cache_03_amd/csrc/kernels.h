@@ -88,6 +88,11 @@ struct FlatArgs {
   int nr;              // ranges (workgroups) per head group
   int max_chunk;       // longest range, in blocks (LDS sizing)
   bool keep_cached;    // normal cache policy for the tiles (blocks shared)
+  // Contiguous layout instead of a block pool: sequence b's token t is row
+  // b * row_tokens + t of k_pool / v_pool ([rows][H][D]); no block tables.
+  bool contig;
+  int row_tokens;
+  const int32_t* capacity;   // contiguous: tokens each sequence may read (or null)
 };
 
 // Grouped decode (pa_decode_grouped.hip): groups of up to kGroupMaxMembers

@@ -132,16 +132,20 @@ struct Tile {
 };
 
 // One (block, head) tile of K and of V through buffer resources covering
-// exactly the two tiles; `lane_off` = lane * 16.
+// the two tiles; load i of a lane reads at lane_off + i * kLoadStride.  In
+// the paged layout lane_off = lane * 16 and the stride is 1024; in a
+// contiguous [token][H][D] layout lane_off = (lane % 16) * row bytes +
+// (lane / 16) * 16 and the stride is 64.  Either way load i of lane l holds
+// token l % 16, dims 8 * (4i + l/16) .. +7.
 // kPolicy: cache-policy bits of the loads (kStreamPolicy or 0).
-template <int D, int kPolicy>
+template <int D, int kPolicy, int kLoadStride = 1024>
 __device__ __forceinline__ void load_tile(Tile<D>& t, rsrc_t kr, rsrc_t vr, uint32_t lane_off) {
 #pragma unroll
   for (int i = 0; i < Geometry<D>::kLoads; ++i)
-    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * 1024, 0, kPolicy);
+    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * kLoadStride, 0, kPolicy);
 #pragma unroll
   for (int i = 0; i < Geometry<D>::kLoads; ++i)
-    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * 1024, 0, kPolicy);
+    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * kLoadStride, 0, kPolicy);
 }
 
 __device__ __forceinline__ h8v as_h8(u4v x) { return __builtin_bit_cast(h8v, x); }

@@ -48,8 +48,14 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int limit) { return min(max(ct
 // s_start[b] = blocks of the sequences before b (b <= B; s_start[B] = T);
 // s_tail[b] (if given) = tokens used in sequence b's last block.  All
 // threads of the workgroup take part; ends with a barrier.
-__device__ void block_prefix(const int32_t* ctx_lens, int B, int ctx_limit, int* s_start,
-                             int* s_tail, int* s_wave) {
+__device__ __forceinline__ int seq_ctx(const int32_t* ctx_lens, const int32_t* capacity, int b,
+                                       int ctx_limit) {
+  const int ctx = clamp_ctx(ctx_lens[b], ctx_limit);
+  return capacity ? min(ctx, max(capacity[b], 0)) : ctx;
+}
+
+__device__ void block_prefix(const int32_t* ctx_lens, const int32_t* capacity, int B,
+                             int ctx_limit, int* s_start, int* s_tail, int* s_wave) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int per = (B + nt - 1) / nt;
@@ -57,7 +63,7 @@ __device__ void block_prefix(const int32_t* ctx_lens, int B, int ctx_limit, int*
   const int hi = min(B, lo + per);
   int own = 0;
   for (int b = lo; b < hi; ++b)
-    own += (clamp_ctx(ctx_lens[b], ctx_limit) + kBlockTokens - 1) / kBlockTokens;
+    own += (seq_ctx(ctx_lens, capacity, b, ctx_limit) + kBlockTokens - 1) / kBlockTokens;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   int incl = own;
@@ -71,7 +77,7 @@ __device__ void block_prefix(const int32_t* ctx_lens, int B, int ctx_limit, int*
   int run = incl - own;
   for (int w = 0; w < wave; ++w) run += s_wave[w];
   for (int b = lo; b < hi; ++b) {
-    const int ctx = clamp_ctx(ctx_lens[b], ctx_limit);
+    const int ctx = seq_ctx(ctx_lens, capacity, b, ctx_limit);
     const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
     s_start[b] = run;
     if (s_tail) s_tail[b] = ctx - (nb - 1) * kBlockTokens;
@@ -136,7 +142,7 @@ __device__ __forceinline__ void store_acc(rsrc_t r, uint32_t off, const float (&
   }
 }
 
-template <int D, int kPolicy>
+template <int D, int kPolicy, bool kContig>
 __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(FlatArgs a) {
   constexpr int kAcc = Geometry<D>::kAcc;
   constexpr int kTile = Geometry<D>::kTileBytes;
@@ -157,7 +163,8 @@ __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(Flat
   const int r = blockIdx.x / a.head_groups;
   const int h = g * a.waves_per_group + wave;
 
-  block_prefix(a.context_lens, a.B, a.ctx_limit, s_start, s_tail, s_wave);
+  block_prefix(a.context_lens, kContig ? a.capacity : nullptr, a.B, a.ctx_limit, s_start, s_tail,
+               s_wave);
   if (blockIdx.x == 0) {               // offsets for the merge kernel
     for (int i = tid; i <= a.B; i += blockDim.x) a.ws_seq[i] = s_start[i];
   }
@@ -168,28 +175,37 @@ __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(Flat
   if (c0 >= c1) return;                // uniform for the workgroup
 
   // Physical block id of every position of the range.
+  // Physical block id of every position of the range; in the contiguous
+  // layout, the index of the sequence's 16-row group instead.
   for (int s = c0 + tid; s < c1; s += blockDim.x) {
     const int b = seq_of(s_start, a.B, s);
-    const int id = a.block_tables[(size_t)b * a.max_blocks + (s - s_start[b])];
-    s_ids[s - c0] = min(max(id, 0), a.num_blocks - 1);
+    if (kContig) {
+      s_ids[s - c0] = b * (a.row_tokens / kBlockTokens) + (s - s_start[b]);
+    } else {
+      const int id = a.block_tables[(size_t)b * a.max_blocks + (s - s_start[b])];
+      s_ids[s - c0] = min(max(id, 0), a.num_blocks - 1);
+    }
   }
   __syncthreads();
 
-  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
-  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
-  const size_t block_stride = (size_t)a.H * kTile;
-  const uint32_t lane_off = lane * 16u;
-  // Past the range's end the load ring still issues its loads (so the load
-  // counters stay exact) but through a zero-size resource: they return 0
-  // without touching memory.
+  // Paged: tile (block, h) at (block * H + h) * kTile, lane l at l * 16.
+  // Contiguous: row r at r * H * D * 2, head h at h * D * 2, lane l at its
+  // token's row plus its 16-byte dim group; a tile spans 16 rows.
+  const size_t row_bytes = (size_t)a.H * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * (kContig ? D * 2 : kTile);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * (kContig ? D * 2 : kTile);
+  const size_t block_stride = kContig ? kBlockTokens * row_bytes : (size_t)a.H * kTile;
+  const uint32_t lane_off = kContig ? (uint32_t)(token * row_bytes) + row * 16u : lane * 16u;
+  const uint32_t tile_span = kContig ? (uint32_t)((kBlockTokens - 1) * row_bytes + D * 2) : kTile;
   // Past the range's end the load ring still issues its loads (so the load
   // counters stay exact) but through a zero-size resource: they return 0
   // without touching memory.
   auto fetch = [&](Tile<D>& t, int s) {
     const int j = min(s, c1 - 1) - c0;
-    const uint32_t bytes = s < c1 ? kTile : 0u;
+    const uint32_t bytes = s < c1 ? tile_span : 0u;
     const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[j]) * block_stride;
-    load_tile<D, kPolicy>(t, make_rsrc(kbase + o, bytes), make_rsrc(vbase + o, bytes), lane_off);
+    load_tile<D, kPolicy, kContig ? 64 : 1024>(t, make_rsrc(kbase + o, bytes),
+                                                make_rsrc(vbase + o, bytes), lane_off);
   };
 
   // Current segment: sequence b, positions [seg_lo, seg_hi) of its
@@ -339,14 +355,20 @@ size_t flat_lds_bytes(int B, int max_chunk) {
 hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream) {
   const size_t lds = flat_lds_bytes(a.B, a.max_chunk);
   const int grid = a.head_groups * a.nr;
-  if (D == 128 && !a.keep_cached)
-    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kStreamPolicy>), dim3(grid), dim3(threads), lds, stream, a);
-  else if (D == 128)
-    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kCachedPolicy>), dim3(grid), dim3(threads), lds, stream, a);
-  else if (!a.keep_cached)
-    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kStreamPolicy>), dim3(grid), dim3(threads), lds, stream, a);
-  else
-    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kCachedPolicy>), dim3(grid), dim3(threads), lds, stream, a);
+  if (a.contig) {
+    if (D == 128)
+      hipLaunchKernelGGL((pa_decode_flat_kernel<128, kStreamPolicy, true>), dim3(grid), dim3(threads), lds, stream, a);
+    else
+      hipLaunchKernelGGL((pa_decode_flat_kernel<64, kStreamPolicy, true>), dim3(grid), dim3(threads), lds, stream, a);
+  } else if (D == 128 && !a.keep_cached) {
+    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kStreamPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+  } else if (D == 128) {
+    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kCachedPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+  } else if (!a.keep_cached) {
+    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kStreamPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+  } else {
+    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kCachedPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int merge_grid = (a.B * a.H + 3) / 4;

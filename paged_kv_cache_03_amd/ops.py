@@ -202,6 +202,111 @@ def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale
     return out
 
 
+class VirtualKV:
+    """A contiguous KV cache in virtual memory with physical chunks mapped
+    on demand (pkv_vkv_* of the C ABI): per layer one K and one V buffer of
+    [max_batch][max_context][H][D] fp16.  Create it with the target device
+    current; ``close()`` (or garbage collection) frees it."""
+
+    def __init__(self, max_batch, max_context, num_layers, num_heads, head_dim,
+                 chunk_bytes=2 << 20):
+        self._lib = _lib.load_library()
+        handle = ctypes.c_void_p()
+        _lib.check("pkv_vkv_create", self._lib.pkv_vkv_create(
+            max_batch, max_context, num_layers, num_heads, head_dim, chunk_bytes,
+            ctypes.byref(handle)))
+        self.handle = handle
+        self.max_batch, self.max_context = max_batch, max_context
+        self.num_layers, self.num_heads, self.head_dim = num_layers, num_heads, head_dim
+
+    def grow(self, seq, tokens):
+        _lib.check("pkv_vkv_grow", self._lib.pkv_vkv_grow(self.handle, seq, tokens))
+
+    def release(self, seq):
+        _lib.check("pkv_vkv_release", self._lib.pkv_vkv_release(self.handle, seq))
+
+    def buffers(self, layer):
+        """(K, V) device addresses of ``layer``'s buffers."""
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _lib.check("pkv_vkv_buffers", self._lib.pkv_vkv_buffers(self.handle, layer,
+                                                                ctypes.byref(k), ctypes.byref(v)))
+        return k.value, v.value
+
+    def capacity_ptr(self):
+        return self._lib.pkv_vkv_capacity(self.handle)
+
+    def stats(self):
+        info = _lib.VkvInfo()
+        _lib.check("pkv_vkv_stats", self._lib.pkv_vkv_stats(self.handle, ctypes.byref(info)))
+        return {name: getattr(info, name) for name, _ in info._fields_}
+
+    def append(self, layer, k, v, seq_ids, positions):
+        """Write row t of k / v ([T][H][D] fp16) as token positions[t] of
+        request seq_ids[t] (int32 device tensors), on the current stream."""
+        _need(k, "k", torch.float16, ndim=3)
+        dev = k.device
+        _need(v, "v", torch.float16, dev, ndim=3)
+        _need(seq_ids, "seq_ids", torch.int32, dev, ndim=1)
+        _need(positions, "positions", torch.int32, dev, ndim=1)
+        T = k.shape[0]
+        if tuple(k.shape) != (T, self.num_heads, self.head_dim) or v.shape != k.shape or \
+                seq_ids.shape[0] != T or positions.shape[0] != T:
+            raise ValueError("k, v, seq_ids, positions do not match")
+        with torch.cuda.device(dev):
+            code = self._lib.pkv_vkv_append(self.handle, layer, _ptr(k), _ptr(v), _ptr(seq_ids),
+                                            _ptr(positions), T, _stream_handle(dev))
+        _lib.check("pkv_vkv_append", code)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self._lib.pkv_vkv_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def contig_decode_workspace_size(batch, num_heads, head_dim, max_context_len):
+    return int(_lib.load_library().pkv_contig_decode_workspace_size(
+        batch, num_heads, head_dim, max_context_len))
+
+
+def contig_decode(q, vkv, layer, context_lens, scale, out=None, *, max_context_len=None,
+                  workspace=None):
+    """``pa_decode`` over the contiguous virtual-memory cache ``vkv``
+    (a VirtualKV): sequence b reads rows b*max_context .. of ``layer``'s
+    buffers, clamped to its mapped tokens."""
+    lib = _lib.load_library()
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    B, H, D = q.shape
+    if B > vkv.max_batch or H != vkv.num_heads or D != vkv.head_dim:
+        raise ValueError("q does not match the virtual cache")
+    _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
+    if context_lens.shape[0] != B:
+        raise ValueError("context_lens does not match the batch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, dev, ndim=3)
+    need = contig_decode_workspace_size(B, H, D, max_context_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    kb, vb = vkv.buffers(layer)
+    with torch.cuda.device(dev):
+        code = lib.pkv_contig_decode(
+            _ptr(q), ctypes.c_void_p(kb), ctypes.c_void_p(vb), vkv.max_context,
+            _ptr(context_lens), ctypes.c_void_p(vkv.capacity_ptr()), max_context_len, B, H, D,
+            float(scale), _ptr(out), _ptr(workspace), workspace.numel(), 0, _stream_handle(dev))
+    _lib.check("pkv_contig_decode", code)
+    return out
+
+
 def kv_append(k, v, slot_mapping, k_pool, v_pool):
     """Write row t of k / v ([T][H][D] fp16) into slot slot_mapping[t]
     (block slot//16, position slot%16) of one layer's pools; negative slots

@@ -259,3 +259,46 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(out=None) == _lib.ERR_NULL_PTR
     assert call(q=A4) == _lib.ERR_MISALIGNED
     assert call(qs=A16 + 2) == _lib.ERR_MISALIGNED
+
+
+def test_contig_decode_rejects_bad_arguments(lib):
+    f = lib.pkv_contig_decode
+
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, L=2048, lens=A16, cap=A16, max_ctx=2048, B=8, H=32, D=128,
+                 scale=0.1, out=A16, ws=A16, ws_bytes=1 << 40, flags=0)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["L"], a["lens"], a["cap"], a["max_ctx"], a["B"],
+                 a["H"], a["D"], a["scale"], a["out"], a["ws"], a["ws_bytes"], a["flags"], None)
+
+    assert call(flags=1) == _lib.ERR_BAD_SHAPE
+    assert call(L=1000) == _lib.ERR_BAD_SHAPE              # not a multiple of 16
+    assert call(L=1024) == _lib.ERR_BAD_SHAPE              # shorter than the longest context
+    assert call(D=32) == _lib.ERR_BAD_SHAPE
+    assert call(B=0, q=None) == _lib.OK
+    assert call(k=None) == _lib.ERR_NULL_PTR
+    assert call(ws=None) == _lib.ERR_NULL_PTR
+    assert call(cap=MIS) == _lib.ERR_MISALIGNED
+    need = lib.pkv_contig_decode_workspace_size(8, 32, 128, 2048)
+    assert need > 0 and call(ws_bytes=need - 1) == _lib.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_vkv_rejects_bad_arguments(lib):
+    h = ctypes.c_void_p()
+    create = lib.pkv_vkv_create
+    assert create(8, 2048, 1, 32, 128, 2 << 20, None) == _lib.ERR_NULL_PTR
+    assert create(8, 2000, 1, 32, 128, 2 << 20, ctypes.byref(h)) == _lib.ERR_BAD_SHAPE
+    assert create(8, 2048, 1, 32, 96, 2 << 20, ctypes.byref(h)) == _lib.ERR_BAD_SHAPE
+    assert create(8, 2048, 0, 32, 128, 2 << 20, ctypes.byref(h)) == _lib.ERR_BAD_SHAPE
+    assert create(8, 2048, 1, 32, 128, 0, ctypes.byref(h)) == _lib.ERR_BAD_SHAPE
+    assert create(8, 2048, 1, 32, 128, 3 << 20, ctypes.byref(h)) == _lib.ERR_BAD_SHAPE  # no divisor
+    assert not h.value
+    assert lib.pkv_vkv_grow(None, 0, 16) == _lib.ERR_NULL_PTR
+    assert lib.pkv_vkv_release(None, 0) == _lib.ERR_NULL_PTR
+    assert lib.pkv_vkv_destroy(None) == _lib.OK
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.pkv_vkv_buffers(None, 0, ctypes.byref(k), ctypes.byref(v)) == _lib.ERR_NULL_PTR
+    assert lib.pkv_vkv_capacity(None) is None
+    info = _lib.VkvInfo()
+    assert lib.pkv_vkv_stats(None, ctypes.byref(info)) == _lib.ERR_NULL_PTR
+    assert lib.pkv_vkv_append(None, 0, A16, A16, A16, A16, 4, None) == _lib.ERR_NULL_PTR

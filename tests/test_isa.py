@@ -40,8 +40,13 @@ def kernel_body(asm, name_part):
 
 
 def meta(asm, name_part, key):
+    """A field of the kernel's own entry in the code-object metadata (the
+    entry runs from its "- .agpr_count" line to the next entry)."""
     sym = re.search(r"^(_Z\S*" + name_part + r"\S*):", asm, re.M).group(1)
-    block = asm[asm.index(f".name:           {sym}") - 2000:asm.index(f".name:           {sym}") + 2000]
+    at = asm.index(f".name:           {sym}")
+    start = asm.rfind("  - .agpr_count:", 0, at)
+    end = asm.find("  - .agpr_count:", at)
+    block = asm[start:end if end > 0 else at + 4000]
     return int(re.search(rf"\.{key}:\s+(\d+)", block).group(1))
 
 
@@ -81,7 +86,7 @@ def tile_loops(body):
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("policy", [2, 0])
 def test_flat_loop_never_drains_loads(flat_asm, D, policy):
-    body = kernel_body(flat_asm, f"pa_decode_flat_kernelILi{D}ELi{policy}E")
+    body = kernel_body(flat_asm, f"pa_decode_flat_kernelILi{D}ELi{policy}ELb0E")
     loops = tile_loops(body)
     assert loops, "no tile loop found"
     for label, text in loops.items():
@@ -104,13 +109,13 @@ def test_partition_loop_never_drains_loads(part_asm, D, policy):
 
 
 def test_no_spills_and_register_budget(flat_asm, part_asm):
-    for asm, name in ((flat_asm, "pa_decode_flat_kernelILi128E"),
+    for asm, name in ((flat_asm, "pa_decode_flat_kernelILi128ELi2ELb0E"),
                       (part_asm, "pa_decode_part_kernelILi128E")):
         assert meta(asm, name, "vgpr_spill_count") == 0
         assert meta(asm, name, "private_segment_fixed_size") == 0
     # two waves per SIMD for the flat kernel (<= 256 VGPRs), three for the
     # partitioned one (<= 168)
-    assert meta(flat_asm, "pa_decode_flat_kernelILi128E", "vgpr_count") <= 256
+    assert meta(flat_asm, "pa_decode_flat_kernelILi128ELi2ELb0E", "vgpr_count") <= 256
     assert meta(part_asm, "pa_decode_part_kernelILi128E", "vgpr_count") <= 168
 
 
@@ -160,3 +165,18 @@ def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D):
     assert waits and min(waits) >= 2 * (D // 32)
     assert meta(prefill_asm, f"pa_prefill_kernelILi{D}E", "vgpr_spill_count") == 0
     assert meta(prefill_asm, f"pa_prefill_kernelILi{D}E", "vgpr_count") <= 256
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_contiguous_flat_loop_never_drains_loads(flat_asm, D):
+    """The same flat kernel addressing contiguous rows: same load ring, no
+    drain, no spill."""
+    name = f"pa_decode_flat_kernelILi{D}ELi2ELb1E"
+    body = kernel_body(flat_asm, name)
+    loops = tile_loops(body)
+    assert loops
+    for label, text in loops.items():
+        assert "vmcnt(0)" not in text, f"full load drain inside loop {label}"
+    assert "vmcnt(0)" not in body[body.index("v_dot2"):]
+    assert meta(flat_asm, name, "vgpr_spill_count") == 0
+    assert meta(flat_asm, name, "vgpr_count") <= 256

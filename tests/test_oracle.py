@@ -451,3 +451,45 @@ def test_prefill_chunks_agree_with_one_pass():
     assert np.array_equal(whole, np.concatenate([first, second]))
     dec = paged_decode_ref(q[19:20], kp, vp, tables, np.array([20]), 0.125)
     assert np.array_equal(first[19], dec[0])
+
+
+# ------------------------------------------------------------ contiguous cache
+
+def test_contiguous_decode_equals_paged_decode():
+    """The same tokens in a contiguous row array and scattered over a block
+    pool through tables give the same decode ("Atenció": the standard
+    attention is kept), bit for bit in float64; rows past a context are
+    never read (NaN there changes nothing)."""
+    from oracle import contiguous_decode_ref
+    rng = np.random.default_rng(35)
+    H, D, L = 3, 64, 96
+    lens = np.array([1, 17, 96, 40, 0], dtype=np.int32)
+    B = len(lens)
+    k_rows = np.full((B * L, H, D), np.nan, dtype=np.float16)
+    v_rows = np.full((B * L, H, D), np.nan, dtype=np.float16)
+    for b, n in enumerate(lens):
+        k_rows[b * L:b * L + n] = rng.standard_normal((n, H, D))
+        v_rows[b * L:b * L + n] = rng.standard_normal((n, H, D))
+    q = rng.standard_normal((B, H, D)).astype(np.float16)
+    out = contiguous_decode_ref(q, k_rows, v_rows, L, lens, 0.125)
+    assert np.isfinite(out).all()
+    # scatter into a pool through shuffled tables, element by element
+    nblk = [-(-int(n) // 16) for n in lens]
+    NB = sum(nblk) + 2
+    ids = rng.permutation(NB)
+    tables = np.full((B, max(nblk)), -1, dtype=np.int32)
+    kp = np.zeros(NB * H * D * 16, dtype=np.float16)
+    vp = np.zeros_like(kp)
+    p = 0
+    for b, n in enumerate(lens):
+        tables[b, :nblk[b]] = ids[p:p + nblk[b]]
+        p += nblk[b]
+        for t in range(int(n)):
+            for h in range(H):
+                for d in range(D):
+                    i = pool_element_index(int(tables[b, t // 16]), h, t % 16, d, H, D)
+                    kp[i] = k_rows[b * L + t, h, d]
+                    vp[i] = v_rows[b * L + t, h, d]
+    shape = wl.pool_shape(NB, H, D)
+    assert np.array_equal(out, paged_decode_ref(q, kp.reshape(shape), vp.reshape(shape), tables,
+                                                lens, 0.125))
