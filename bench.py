@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = default)")
     ap.add_argument("--workload", default="batch200",
                     choices=["batch200", "batch10", "shared_prefix", "full_step", "beam_step",
-                             "prefill_prompt", "prefill_chunked"],
+                             "prefill_prompt", "prefill_chunked", "vattention"],
                     help="batch200 (default): the headline one-layer batch of 200")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0,
@@ -49,6 +49,8 @@ def parse():
                     help="decode entry point: pa_decode (flat strategy unless --partition) or "
                          "pa_decode_grouped (each shared block read once per group); auto = "
                          "grouped for the workloads whose tables share blocks")
+    ap.add_argument("--vkv-chunk", type=int, default=2 << 20,
+                    help="vattention workload: bytes of physical memory mapped at a time")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic record from two rocprofv3 counter_collection "
                          "CSVs (FETCH_SIZE pass, WRITE_SIZE pass; both runs with --copy-probe) "
@@ -389,6 +391,126 @@ def setup_full_step(torch, dev, wl, args, beams):
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
 
 
+def setup_vattention(torch, dev, wl, args):
+    """The headline batch (200 sequences, one layer) on a contiguous KV cache
+    in virtual memory with physical chunks mapped on demand (the vAttention
+    alternative): per step one new token per sequence is written into its
+    row and the contiguous decode runs.  The paged step on the same data is
+    timed alongside, and the physical memory of both layouts is reported."""
+    import time as _time
+
+    import numpy as np
+    from paged_kv_cache_03_amd import (VirtualKV, contig_decode, contig_decode_workspace_size,
+                                       pa_decode)
+    case = wl.gpt_batch(200, seed=2, append=True, fill=False)
+    B, H, D, L = case.batch, case.num_heads, case.head_dim, 2048
+    row = H * D * 2
+    kp = wl.device_pool(torch, case, 0, 0, dev)
+    vp = wl.device_pool(torch, case, 0, 1, dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    q, lens, tables = t(case.q), t(case.context_lens), t(case.block_tables)
+    vkv = VirtualKV(B, L, 1, H, D, chunk_bytes=args.vkv_chunk)
+    t0 = _time.perf_counter()
+    for b, n in enumerate(case.context_lens):
+        vkv.grow(b, int(n))
+    grow_s = _time.perf_counter() - t0
+    # cached tokens (all but the last) copied from the paged pools
+    NB = case.num_blocks
+    tok = lambda pool: pool.view(NB, H, D // 8, 16, 8).permute(0, 3, 1, 2, 4).reshape(NB, 16, H, D)
+    seq = np.concatenate([np.full(int(n) - 1, b, dtype=np.int32) for b, n in enumerate(case.context_lens)])
+    pos = np.concatenate([np.arange(int(n) - 1, dtype=np.int32) for n in case.context_lens])
+    blk = torch.from_numpy(case.block_tables[seq, pos // 16].astype(np.int64)).to(dev)
+    slot = torch.from_numpy((pos % 16).astype(np.int64)).to(dev)
+    vkv.append(0, tok(kp)[blk, slot].contiguous(), tok(vp)[blk, slot].contiguous(), t(seq), t(pos))
+    torch.cuda.synchronize()
+    new_seq = t(np.arange(B, dtype=np.int32))
+    new_pos = t((case.context_lens - 1).astype(np.int32))
+    kn, vn = t(case.k_new), t(case.v_new)
+    out = torch.empty_like(q)
+    ws = torch.empty(contig_decode_workspace_size(B, H, D, case.max_context), dtype=torch.uint8,
+                     device=dev)
+
+    def step(events):
+        vkv.append(0, kn, vn, new_seq, new_pos)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+        contig_decode(q, vkv, 0, lens, case.scale, out, max_context_len=case.max_context,
+                      workspace=ws)
+        events.append(torch.cuda.Event(enable_timing=True))
+        events[-1].record()
+
+    # the paged decode on the same tokens, for comparison
+    ref_out = torch.empty_like(q)
+    for _ in range(5):
+        pa_decode(q, kp, vp, tables, lens, case.scale, ref_out, max_context_len=case.max_context)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(50):
+        pa_decode(q, kp, vp, tables, lens, case.scale, ref_out, max_context_len=case.max_context)
+    e.record()
+    torch.cuda.synchronize()
+    paged_us = s.elapsed_time(e) / 50 * 1e3
+
+    # the same rows in one ordinary allocation: the layout without the mapping
+    from paged_kv_cache_03_amd import contig_decode_rows
+    rows = torch.from_numpy(seq.astype(np.int64) * L + pos).to(dev)
+    k_rows = torch.zeros((B * L, H, D), dtype=torch.float16, device=dev)
+    v_rows = torch.zeros_like(k_rows)
+    k_rows.index_copy_(0, rows, tok(kp)[blk, slot])
+    v_rows.index_copy_(0, rows, tok(vp)[blk, slot])
+    last = torch.from_numpy(np.arange(B, dtype=np.int64) * L + case.context_lens - 1).to(dev)
+    k_rows.index_copy_(0, last, kn)
+    v_rows.index_copy_(0, last, vn)
+    for _ in range(5):
+        contig_decode_rows(q, k_rows, v_rows, L, lens, case.scale, ref_out,
+                           max_context_len=case.max_context, workspace=ws)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(50):
+        contig_decode_rows(q, k_rows, v_rows, L, lens, case.scale, ref_out,
+                           max_context_len=case.max_context, workspace=ws)
+    e.record()
+    torch.cuda.synchronize()
+    plain_us = s.elapsed_time(e) / 50 * 1e3
+    del k_rows, v_rows
+
+    st = vkv.stats()
+    ctx = case.context_lens.astype(np.int64)
+    r16 = (ctx + 15) // 16 * 16
+    mapped_at = lambda c: int(((r16 * row + c - 1) // c * c).sum()) * 2
+    paged_bytes = int(((ctx + 15) // 16).sum()) * 16 * row * 2
+    kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
+    written = int(ctx.sum()) * row * 2
+    extra = {
+        "decode": "pkv_contig_decode (contiguous rows in virtual memory)",
+        "paged_decode_us_same_tokens": round(paged_us, 3),
+        "contig_decode_us_ordinary_allocation": round(plain_us, 3),
+        "memory": {
+            "written_kv_bytes": written,
+            "paged_16_token_blocks_bytes": paged_bytes,
+            "virtual_mapped_bytes": int(st["mapped_bytes"]),
+            "virtual_chunk_bytes": int(st["chunk_bytes"]),
+            "virtual_mapped_bytes_by_chunk": {str(c): mapped_at(c)
+                                              for c in (64 << 10, 256 << 10, 2 << 20)},
+            "naive_max_context_bytes": B * L * row * 2,
+            "reserved_virtual_bytes": int(st["reserved_bytes"]),
+        },
+        "mapping": {"granularity": int(st["granularity"]), "map_calls": int(st["map_calls"]),
+                    "us_per_map_call": round(1e6 * st["map_seconds"] / max(st["map_calls"], 1), 1),
+                    "grow_all_s": round(grow_s, 4)},
+    }
+    return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
+               algo_bytes=algo_bytes, strategy="contiguous", part=0, extra=extra, vkv=vkv,
+               config={"workload": "one layer, batch 200, 32 heads x 128 dims fp16, contexts "
+                                   "prompt U[32,256] + geometric(mean 500) capped at 2048, in a "
+                                   "contiguous virtual-memory cache mapped in "
+                                   f"{args.vkv_chunk} B chunks; per step append of 1 "
+                                   "token/sequence + contiguous decode",
+                       "batch": B, "heads": H, "head_dim": D, "max_context": L,
+                       "context_tokens": case.kv_tokens(), "seed": 2})
+
+
 def setup_prefill(torch, dev, wl, args, chunked):
     """One layer of prefill: per step the new tokens' keys and values are
     appended through their slots, then every new token attends causally over
@@ -466,6 +588,8 @@ def main():
         run = setup_batch(torch, dev, wl, args, 10, 1)
     elif args.workload == "shared_prefix":
         run = setup_shared_prefix(torch, dev, wl, args)
+    elif args.workload == "vattention":
+        run = setup_vattention(torch, dev, wl, args)
     elif args.workload.startswith("prefill"):
         run = setup_prefill(torch, dev, wl, args, args.workload == "prefill_chunked")
     else:

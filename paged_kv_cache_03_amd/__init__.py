@@ -12,7 +12,9 @@ copy pairs.
 from ._lib import LIB_PATH, LibraryMissing, PagedKVError, load_library  # noqa: F401
 from .blocks import (PAGE_TOKENS, PagedRequest, PagePool, PoolExhausted,  # noqa: F401
                      decode_groups, device_arrays, kv_bytes_per_token, tables_share_blocks)
-from .ops import (VirtualKV, contig_decode, cow_copy_blocks, default_partition,  # noqa: F401
+from .ops import (VirtualKV, contig_decode, contig_decode_rows,  # noqa: F401
+                  contig_decode_workspace_size,
+                  cow_copy_blocks, default_partition,
                   kv_append, pa_decode,
                   pa_decode_grouped, pa_decode_grouped_workspace_size, pa_decode_workspace_size,
                   pa_prefill, pool_shape)

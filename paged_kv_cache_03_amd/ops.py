@@ -274,17 +274,11 @@ def contig_decode_workspace_size(batch, num_heads, head_dim, max_context_len):
         batch, num_heads, head_dim, max_context_len))
 
 
-def contig_decode(q, vkv, layer, context_lens, scale, out=None, *, max_context_len=None,
-                  workspace=None):
-    """``pa_decode`` over the contiguous virtual-memory cache ``vkv``
-    (a VirtualKV): sequence b reads rows b*max_context .. of ``layer``'s
-    buffers, clamped to its mapped tokens."""
+def _contig_call(q, k_addr, v_addr, row_tokens, context_lens, capacity_addr, scale, out,
+                 max_context_len, workspace):
     lib = _lib.load_library()
-    _need(q, "q", torch.float16, ndim=3)
     dev = q.device
     B, H, D = q.shape
-    if B > vkv.max_batch or H != vkv.num_heads or D != vkv.head_dim:
-        raise ValueError("q does not match the virtual cache")
     _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
     if context_lens.shape[0] != B:
         raise ValueError("context_lens does not match the batch")
@@ -293,18 +287,54 @@ def contig_decode(q, vkv, layer, context_lens, scale, out=None, *, max_context_l
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", torch.float16, dev, ndim=3)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B][H][D]")
     need = contig_decode_workspace_size(B, H, D, max_context_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev)
-    kb, vb = vkv.buffers(layer)
     with torch.cuda.device(dev):
         code = lib.pkv_contig_decode(
-            _ptr(q), ctypes.c_void_p(kb), ctypes.c_void_p(vb), vkv.max_context,
-            _ptr(context_lens), ctypes.c_void_p(vkv.capacity_ptr()), max_context_len, B, H, D,
+            _ptr(q), ctypes.c_void_p(k_addr), ctypes.c_void_p(v_addr), row_tokens,
+            _ptr(context_lens), ctypes.c_void_p(capacity_addr), max_context_len, B, H, D,
             float(scale), _ptr(out), _ptr(workspace), workspace.numel(), 0, _stream_handle(dev))
     _lib.check("pkv_contig_decode", code)
     return out
+
+
+def contig_decode(q, vkv, layer, context_lens, scale, out=None, *, max_context_len=None,
+                  workspace=None):
+    """``pa_decode`` over the contiguous virtual-memory cache ``vkv``
+    (a VirtualKV): sequence b reads rows b*max_context .. of ``layer``'s
+    buffers, clamped to its mapped tokens."""
+    _need(q, "q", torch.float16, ndim=3)
+    B, H, D = q.shape
+    if B > vkv.max_batch or H != vkv.num_heads or D != vkv.head_dim:
+        raise ValueError("q does not match the virtual cache")
+    kb, vb = vkv.buffers(layer)
+    return _contig_call(q, kb, vb, vkv.max_context, context_lens, vkv.capacity_ptr(), scale, out,
+                        max_context_len, workspace)
+
+
+def contig_decode_rows(q, k_rows, v_rows, row_tokens, context_lens, scale, out=None, *,
+                       capacity=None, max_context_len=None, workspace=None):
+    """``pa_decode`` over contiguous K/V rows in ordinary tensors
+    ([B*row_tokens][H][D] fp16): sequence b's token t is row
+    b*row_tokens + t; ``capacity`` (int32 [B], optional) clamps the
+    contexts."""
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    B, H, D = q.shape
+    for name, t in (("k_rows", k_rows), ("v_rows", v_rows)):
+        _need(t, name, torch.float16, dev, ndim=3)
+        if tuple(t.shape[1:]) != (H, D) or t.shape[0] < B * row_tokens:
+            raise ValueError(f"{name} must hold B*row_tokens rows of [H][D]")
+    cap = 0
+    if capacity is not None:
+        _need(capacity, "capacity", torch.int32, dev, ndim=1)
+        cap = capacity.data_ptr()
+    return _contig_call(q, k_rows.data_ptr(), v_rows.data_ptr(), row_tokens, context_lens, cap,
+                        scale, out, max_context_len, workspace)
 
 
 def kv_append(k, v, slot_mapping, k_pool, v_pool):
