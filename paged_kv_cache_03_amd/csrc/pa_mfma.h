@@ -14,8 +14,8 @@
 //  * O^T (D x 16 queries) += V^T (D x 16 tokens) . P^T (16 tokens x 16
 //    queries), one v_mfma_f32_16x16x16_f16 per 16 output dims.  P^T is the
 //    score result's own layout; V^T is read back transposed from the wave's
-//    LDS copy of the V tile.  acc[s] lane l: dims 16s + 4*tg + r of query
-//    l%16.
+//    LDS copy of the V tile with the gfx950 transpose read.  acc[s] lane l:
+//    dims 16s + 4*tg + r of query l%16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -100,13 +100,19 @@ __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D
     w.w = tok_ok ? w.w : 0u;
     sv[i * kWave + lane] = w;
   }
+  // V^T for slice s with ds_read_b64_tr_b16: within each group of 16 lanes
+  // it returns to lane j, element e, element j%4 of the 8 bytes addressed by
+  // lane j/4 + 4e.  Lane i (= qc) of group tg therefore addresses dims
+  // 16s + 4*(i%4) .. +3 of token 4*tg + i/4 (8 aligned bytes of the tile's
+  // [D/8][16][8] layout), and receives V[4*tg + e][16s + i], e < 4: the A
+  // operand (row = dim, k = token).
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  const int tr_base = (((qc & 3) >> 1) * kBlockTokens + 4 * tg + (qc >> 2)) * 8 + 4 * (qc & 1);
 #pragma unroll
   for (int s = 0; s < kS; ++s) {
-    const int d = 16 * s + qc;
-    const int base = ((d >> 3) * kBlockTokens + 4 * tg) * 8 + (d & 7);
-    h4v va;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) va[e] = svh[base + e * 8];
+    const s4v raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4v*)(svh + tr_base + s * 2 * kBlockTokens * 8));
+    const h4v va = __builtin_bit_cast(h4v, raw);
     acc[s] = acc[s] * alpha;
     acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[s], 0, 0, 0);
   }
