@@ -400,9 +400,8 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   const int32_t blocks_used = ceil_div(max_context_len, kBlockTokens);
   if (pkv::prefill_lds_bytes(B, blocks_used) > (size_t)pkv::kPrefillMaxLdsBytes)
     return PKV_ERR_BAD_SHAPE;
-  const int32_t head_groups = (H + pkv::kPrefillWaves - 1) / pkv::kPrefillWaves;
-  // tiles: sum over sequences of ceil(n_b / 16) <= num_query_rows / 16 + B
-  const long long grid = ((long long)ceil_div(num_query_rows, 16) + B) * head_groups;
+  // query groups: sum over sequences of ceil(n_b / 64) <= num_query_rows / 64 + B
+  const long long grid = ((long long)ceil_div(num_query_rows, pkv::kPrefillRows) + B) * H;
   if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out)
     return PKV_ERR_NULL_PTR;
@@ -424,7 +423,6 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = max_context_len;
   a.num_blocks = num_blocks;
-  a.head_groups = head_groups;
   const hipError_t e = pkv::launch_pa_prefill(a, D, (int)grid, blocks_used,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -135,9 +135,10 @@ struct GroupArgs {
   bool keep_cached;
 };
 
-// Prefill (pa_prefill.hip): one workgroup per (16-query tile, head group).
-constexpr int kPrefillWaves = 4;           // waves (heads) per workgroup
-constexpr int kPrefillTiles = 3;           // tiles in each wave's load ring
+// Prefill (pa_prefill.hip): one workgroup per (64 query rows, head).
+constexpr int kPrefillWaves = 4;           // waves per workgroup, 16 query rows each
+constexpr int kPrefillRows = 16 * kPrefillWaves;
+constexpr int kPrefillTiles = 4;           // tiles in the workgroup's load ring (even)
 constexpr int kPrefillMaxLdsBytes = 32 * 1024;
 
 struct PrefillArgs {
@@ -154,7 +155,6 @@ struct PrefillArgs {
   int max_blocks;
   int ctx_limit;
   int num_blocks;
-  int head_groups;              // ceil(H / kPrefillWaves)
 };
 
 struct AppendArgs {

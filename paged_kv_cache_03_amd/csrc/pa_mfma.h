@@ -53,25 +53,21 @@ __device__ __forceinline__ void mfma_fetch(MTile<D>& t, rsrc_t kr, rsrc_t vr, ui
     t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * 1024, 0, kPolicy);
 }
 
-// One tile.  live(tok) says whether token tok (0..15 of the tile) is
-// attended by this lane's query column; tokens at or past `valid` hold no
-// data and must not be live (their V rows are zeroed: they may hold
-// anything, NaN included, and weight 0 * NaN would still be NaN).
-// sv / svh: the wave's own LDS area of D * 16 fp16 (the wave's LDS
-// operations run in order, so no barrier is needed).
+// Scores and online-softmax step of one tile: k[i] are the K tile's A
+// operands (lane l: token l%16, dims 32i + 8*tg ..).  live(tok) says whether
+// token tok (0..15 of the tile) is attended by this lane's query column.
+// Returns the rescale factor of the running sums; pb receives the fp16
+// weights of this lane's tokens 4*tg + r (the P^T operand).
 template <int D, typename Live>
-__device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D / 32],
-                                            float scale_log2, int valid, Live live, float& m,
-                                            float& l, f4v (&acc)[D / 16], u4v* sv,
-                                            const _Float16* svh, int lane) {
+__device__ __forceinline__ float mfma_scores(const u4v (&k)[D / 32], const h8v (&qb)[D / 32],
+                                             float scale_log2, Live live, float& m, float& l,
+                                             h4v& pb, int lane) {
   constexpr int kK = D / 32;
-  constexpr int kS = D / 16;
-  const int qc = lane % 16;
   const int tg = lane / 16;
   f4v sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < kK; ++i)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(t.k[i]), qb[i], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(k[i]), qb[i], sc, 0, 0, 0);
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -81,7 +77,6 @@ __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D
   const float mnew = fmaxf(m, cross_row_max(mx));
   const float mref = mnew == kNegInf ? 0.0f : mnew;
   const float alpha = exp2f(m - mref);
-  h4v pb;
   float psum = 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -90,9 +85,49 @@ __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D
   }
   l = fmaf(l, alpha, psum);
   m = mnew;
-  const bool tok_ok = qc < valid;      // this lane's loaded token is l % 16
+  return alpha;
+}
+
+// P.V step of one tile: vt points at the tile's V in LDS, in the tile's own
+// [D/8][16][8] layout, with the slots past the context already zeroed.
+// V^T for slice s comes from ds_read_b64_tr_b16: within each group of 16
+// lanes it returns to lane j, element e, element j%4 of the 8 bytes
+// addressed by lane j/4 + 4e.  Lane i (= l%16) of group tg therefore
+// addresses dims 16s + 4*(i%4) .. +3 of token 4*tg + i/4 (8 aligned bytes),
+// and receives V[4*tg + e][16s + i], e < 4: the A operand (row = dim, k =
+// token).
+template <int D>
+__device__ __forceinline__ void mfma_pv(f4v (&acc)[D / 16], float alpha, h4v pb,
+                                        const _Float16* vt, int lane) {
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  const int qc = lane % 16;
+  const int tg = lane / 16;
+  const int tr_base = (((qc & 3) >> 1) * kBlockTokens + 4 * tg + (qc >> 2)) * 8 + 4 * (qc & 1);
 #pragma unroll
-  for (int i = 0; i < kK; ++i) {
+  for (int s = 0; s < D / 16; ++s) {
+    const s4v raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4v*)(vt + tr_base + s * 2 * kBlockTokens * 8));
+    const h4v va = __builtin_bit_cast(h4v, raw);
+    acc[s] = acc[s] * alpha;
+    acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[s], 0, 0, 0);
+  }
+}
+
+// One tile held in the wave's registers.  Tokens at or past `valid` hold no
+// data and must not be live; their V rows are zeroed before use (they may
+// hold anything, NaN included, and weight 0 * NaN would still be NaN).
+// sv / svh: the wave's own LDS area of D * 16 fp16 (the wave's LDS
+// operations run in order, so no barrier is needed).
+template <int D, typename Live>
+__device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D / 32],
+                                            float scale_log2, int valid, Live live, float& m,
+                                            float& l, f4v (&acc)[D / 16], u4v* sv,
+                                            const _Float16* svh, int lane) {
+  h4v pb;
+  const float alpha = mfma_scores<D>(t.k, qb, scale_log2, live, m, l, pb, lane);
+  const bool tok_ok = lane % 16 < valid;     // this lane's loaded token is l % 16
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
     u4v w = t.v[i];
     w.x = tok_ok ? w.x : 0u;
     w.y = tok_ok ? w.y : 0u;
@@ -100,22 +135,7 @@ __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D
     w.w = tok_ok ? w.w : 0u;
     sv[i * kWave + lane] = w;
   }
-  // V^T for slice s with ds_read_b64_tr_b16: within each group of 16 lanes
-  // it returns to lane j, element e, element j%4 of the 8 bytes addressed by
-  // lane j/4 + 4e.  Lane i (= qc) of group tg therefore addresses dims
-  // 16s + 4*(i%4) .. +3 of token 4*tg + i/4 (8 aligned bytes of the tile's
-  // [D/8][16][8] layout), and receives V[4*tg + e][16s + i], e < 4: the A
-  // operand (row = dim, k = token).
-  typedef short s4v __attribute__((ext_vector_type(4)));
-  const int tr_base = (((qc & 3) >> 1) * kBlockTokens + 4 * tg + (qc >> 2)) * 8 + 4 * (qc & 1);
-#pragma unroll
-  for (int s = 0; s < kS; ++s) {
-    const s4v raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s4v*)(svh + tr_base + s * 2 * kBlockTokens * 8));
-    const h4v va = __builtin_bit_cast(h4v, raw);
-    acc[s] = acc[s] * alpha;
-    acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, acc[s], 0, 0, 0);
-  }
+  mfma_pv<D>(acc, alpha, pb, svh, lane);
 }
 
 }  // namespace dev
