@@ -113,6 +113,66 @@ __device__ __forceinline__ void mfma_pv(f4v (&acc)[D / 16], float alpha, h4v pb,
   }
 }
 
+// Two tiles a, b (32 tokens) at once, for the P.V product on the full-rate
+// v_mfma_f32_16x16x32_f16: its 32 k slots are ordered so that lane quarter
+// tg's 8 slots are tokens 4*tg .. 4*tg+3 of tile a, then the same tokens of
+// tile b.  The P^T operand is then the two score results side by side, and
+// V^T is two transpose reads (one per tile) side by side; the order is the
+// same for both operands, so the product is the plain sum over the 32
+// tokens.  live_a / live_b: as `live` of mfma_scores for each tile.
+template <int D, typename LiveA, typename LiveB>
+__device__ __forceinline__ void mfma_update_pair(const u4v (&ka)[D / 32], const u4v (&kb)[D / 32],
+                                                 const h8v (&qb)[D / 32], float scale_log2,
+                                                 LiveA live_a, LiveB live_b, float& m, float& l,
+                                                 f4v (&acc)[D / 16], const _Float16* vta,
+                                                 const _Float16* vtb, int lane) {
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef short s8v __attribute__((ext_vector_type(8)));
+  constexpr int kK = D / 32;
+  const int qc = lane % 16;
+  const int tg = lane / 16;
+  f4v sa = {0.0f, 0.0f, 0.0f, 0.0f};
+  f4v sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kK; ++i) {
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(ka[i]), qb[i], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kb[i]), qb[i], sb, 0, 0, 0);
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sa[r] = live_a(4 * tg + r) ? sa[r] * scale_log2 : kNegInf;
+    sb[r] = live_b(4 * tg + r) ? sb[r] * scale_log2 : kNegInf;
+    mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
+  }
+  const float mnew = fmaxf(m, cross_row_max(mx));
+  const float mref = mnew == kNegInf ? 0.0f : mnew;
+  const float alpha = exp2f(m - mref);
+  h8v pb;
+  float psum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pb[r] = (_Float16)exp2f(sa[r] - mref);
+    pb[4 + r] = (_Float16)exp2f(sb[r] - mref);
+    psum += (float)pb[r] + (float)pb[4 + r];
+  }
+  l = fmaf(l, alpha, psum);
+  m = mnew;
+  const int tr_base = (((qc & 3) >> 1) * kBlockTokens + 4 * tg + (qc >> 2)) * 8 + 4 * (qc & 1);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int off = tr_base + s * 2 * kBlockTokens * 8;
+    const s4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4v*)(vta + off));
+    const s4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4v*)(vtb + off));
+    const s8v both = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+    acc[s] = acc[s] * alpha;
+    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v, both), pb, acc[s],
+                                                    0, 0, 0);
+  }
+}
+
 // One tile held in the wave's registers.  Tokens at or past `valid` hold no
 // data and must not be live; their V rows are zeroed before use (they may
 // hold anything, NaN included, and weight 0 * NaN would still be NaN).

@@ -12,9 +12,11 @@
 // The workgroup streams the blocks up to the one holding its last row's
 // position once: every (block, head) tile of K and V is fetched by all 256
 // threads together (32 bytes each) through a register ring of kPrefillTiles
-// tiles, stored into one of two LDS stages (V slots past the context
-// zeroed), and after one barrier read by all 4 waves: K as the scores'
-// A operands, V through the transpose read as the P.V operand (pa_mfma.h).
+// tiles and stored into one of four LDS stages (V slots past the context
+// zeroed); after every second tile a barrier, then all 4 waves consume the
+// pair: K as the scores' A operands, V through the transpose read, and the
+// P.V product over 32 tokens at once on the full-rate 16x16x32 MFMA
+// (pa_mfma.h).
 // Blocks past a row's position are exact no-ops for it (causal mask per
 // element), so a row's result does not depend on the rows it shares a
 // workgroup with.  Workgroup i serves head i % H (one XCD per head when H is
@@ -91,10 +93,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillA
   constexpr int kTileUnits = kTile / 16;                // 16-byte units of one tile
   constexpr int kUnits = 2 * kTileUnits / (64 * kPrefillWaves);   // per thread: K and V
   constexpr int R = kPrefillTiles;
-  static_assert(kUnits >= 1 && R % 2 == 0, "tile split and stage parity");
+  static_assert(kUnits >= 1 && R == 4, "tile split; four stages, consumed in pairs");
   extern __shared__ int smem[];
   __shared__ int s_wave[kPrefillWaves];
-  __shared__ u4v s_kv[2][2 * kTileUnits];               // stage: K tile, then V tile
+  __shared__ u4v s_kv[R][2 * kTileUnits];               // stage: K tile, then V tile
   int* s_group = smem;                                  // B + 1
   int* s_ids = smem + a.B + 1;                          // block ids of the sequence
 
@@ -178,20 +180,28 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillA
         s_kv[st][(unit_is_v(k) ? kTileUnits : 0) + tid % kTileUnits] = w;
       }
     };
-    auto compute = [&](int st, int j) {
-      const int valid = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
+    // two tiles per step: j and j + 1 from stages sa and sa + 1
+    auto compute = [&](int sa, int j) {
+      const int va = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
+      const int vb = j + 1 < nblk ? min(kBlockTokens, ctx - (j + 1) * kBlockTokens) : 0;
       const int t0 = j * kBlockTokens;
-      u4v kt[kK];
+      u4v ka[kK], kb[kK];
 #pragma unroll
-      for (int i = 0; i < kK; ++i) kt[i] = s_kv[st][i * kWave + lane];
-      h4v pb;
-      const float alpha = mfma_scores<D>(
-          kt, qb, a.scale_log2, [&](int tok) { return row_ok && tok < valid && t0 + tok <= p_q; },
-          m, l, pb, lane);
-      mfma_pv<D>(acc, alpha, pb, reinterpret_cast<const _Float16*>(&s_kv[st][kTileUnits]), lane);
+      for (int i = 0; i < kK; ++i) {
+        ka[i] = s_kv[sa][i * kWave + lane];
+        kb[i] = s_kv[sa + 1][i * kWave + lane];
+      }
+      mfma_update_pair<D>(
+          ka, kb, qb, a.scale_log2,
+          [&](int tok) { return row_ok && tok < va && t0 + tok <= p_q; },
+          [&](int tok) { return row_ok && tok < vb && t0 + kBlockTokens + tok <= p_q; },
+          m, l, acc, reinterpret_cast<const _Float16*>(&s_kv[sa][kTileUnits]),
+          reinterpret_cast<const _Float16*>(&s_kv[sa + 1][kTileUnits]), lane);
     };
-    // R tiles in flight; steps past the last block see valid = 0 (exact
-    // no-ops), so the loop runs whole rounds with no exit in its body.
+    // R tiles in flight, four LDS stages: tiles j0 .. j0+3 of a round go to
+    // stages 0 .. 3, a barrier after each pair, then the pair is consumed.
+    // Steps past the last block see valid = 0 (exact no-ops), so the loop
+    // runs whole rounds with no exit in its body.
     u4v ring[R][kUnits];
 #pragma unroll
     for (int r = 0; r + 1 < R; ++r) fetch(ring[r], r);
@@ -199,9 +209,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillA
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         fetch(ring[(r + R - 1) % R], j + r + R - 1);
-        stage(ring[r], r % 2, j + r);
-        __syncthreads();
-        compute(r % 2, j + r);
+        stage(ring[r], r, j + r);
+        if (r % 2 == 1) {
+          __syncthreads();
+          compute(r - 1, j + r - 1);
+        }
       }
     }
   }
