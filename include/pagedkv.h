@@ -248,9 +248,11 @@ size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,
  *   out[r][h] = sum_{t <= p} softmax_t(scale * q[r][h] . K_t) * V_t,
  *
  * with K_t / V_t read through block_tables[b] as for pkv_pa_decode (fp32
- * arithmetic on the matrix cores, probabilities rounded to fp16 before the
- * value product, fp16 output with round to nearest even).  Rows at a
- * negative position (n_b > context_lens[b]) are zero rows.
+ * arithmetic on the matrix cores; online softmax whose reference maximum is
+ * raised only when a score exceeds it by more than 8 (log2 units), so the
+ * fp16 weights stay below 256; the running sum adds the rounded weights;
+ * fp16 output with round to nearest even).  Rows at a negative position
+ * (n_b > context_lens[b]) are zero rows.  Any finite scale, of either sign.
  *
  * device: q and out [num_query_rows][H][D] fp16 (16-byte aligned), k_pool,
  *         v_pool, block_tables, context_lens, query_start (B + 1 entries,

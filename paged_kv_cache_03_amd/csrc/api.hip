@@ -400,7 +400,7 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   const int32_t blocks_used = ceil_div(max_context_len, kBlockTokens);
   if (pkv::prefill_lds_bytes(B, blocks_used) > (size_t)pkv::kPrefillMaxLdsBytes)
     return PKV_ERR_BAD_SHAPE;
-  // query groups: sum over sequences of ceil(n_b / 64) <= num_query_rows / 64 + B
+  // query groups: sum over sequences of ceil(n_b / R) <= num_query_rows / R + B, R = kPrefillRows
   const long long grid = ((long long)ceil_div(num_query_rows, pkv::kPrefillRows) + B) * H;
   if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out)

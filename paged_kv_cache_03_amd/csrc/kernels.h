@@ -135,10 +135,16 @@ struct GroupArgs {
   bool keep_cached;
 };
 
-// Prefill (pa_prefill.hip): one workgroup per (64 query rows, head).
-constexpr int kPrefillWaves = 4;           // waves per workgroup, 16 query rows each
-constexpr int kPrefillRows = 16 * kPrefillWaves;
-constexpr int kPrefillTiles = 4;           // tiles in the workgroup's load ring (even)
+// Prefill (pa_prefill.hip): one workgroup per (128 query rows, head).
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4
+#endif
+#ifndef PKV_PREFILL_TILES
+#define PKV_PREFILL_TILES 4
+#endif
+constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, 32 query rows each
+constexpr int kPrefillRows = 32 * kPrefillWaves;
+constexpr int kPrefillTiles = PKV_PREFILL_TILES;   // tiles in flight + 1 (a multiple of 4)
 constexpr int kPrefillMaxLdsBytes = 32 * 1024;
 
 struct PrefillArgs {

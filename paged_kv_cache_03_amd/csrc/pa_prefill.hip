@@ -7,16 +7,29 @@
 // token sees the tokens up to and including its own position.  Query row i
 // of sequence b (n_b rows) sits at position ctx_b - n_b + i.
 //
-// Work: a workgroup takes 64 consecutive query rows of one sequence for one
-// head; each of its 4 waves serves 16 of them, one MFMA column per row.
-// The workgroup streams the blocks up to the one holding its last row's
-// position once: every (block, head) tile of K and V is fetched by all 256
-// threads together (32 bytes each) through a register ring of kPrefillTiles
-// tiles and stored into one of four LDS stages (V slots past the context
-// zeroed); after every second tile a barrier, then all 4 waves consume the
-// pair: K as the scores' A operands, V through the transpose read, and the
-// P.V product over 32 tokens at once on the full-rate 16x16x32 MFMA
-// (pa_mfma.h).
+// Work: a workgroup takes 128 consecutive query rows of one sequence for
+// one head; each of its 4 waves serves 32 of them.  The workgroup streams
+// the blocks up to the one holding its last row's position once: every
+// (block, head) tile of K and V is fetched by the workgroup's threads
+// together (16 bytes each) through a register ring of kPrefillTiles tiles
+// and stored into one of four LDS stages (V slots past the context zeroed,
+// V token slots swizzled against bank conflicts); after every second tile a
+// barrier, then each wave consumes the pair (32 tokens) on the
+// v_mfma_f32_32x32x16_f16 matrix instruction, whose lane l holds row l%32
+// and k slots 8*(l/32) .. +7 of A, the same of B (column l%32), and C rows
+// 8*(r/4) + 4*(l/32) + r%4 of column l%32 in its register r:
+//  * scores S^T (32 tokens x 32 queries) = K . Q^T, one MFMA per 16 dims:
+//    lane l reads the 16 bytes of token l%32 (tile (l%32)/16), dims
+//    16i + 8*(l/32) .. +7 from LDS as its A operand; the queries are the B
+//    operand, loaded once;
+//  * online softmax per query column: a query's 32 scores sit in lanes c and
+//    c + 32 (16 each), combined with one permlane32 swap; the weights are
+//    rounded to fp16 once and the running sum uses the rounded weights;
+//  * O^T (D x 32 queries) += V^T . P^T, per 32 output dims one MFMA per tile:
+//    its k slot 8h + e (h = l/32) is token 4h + e%4 + 8*(e/4) of the tile,
+//    which is exactly score registers 8kk .. 8kk+7 (kk = the tile), so P^T
+//    is the score result itself; V^T comes from two transpose reads (tokens
+//    4h .. 4h+3 and 8+4h .. 8+4h+3).
 // Blocks past a row's position are exact no-ops for it (causal mask per
 // element), so a row's result does not depend on the rows it shares a
 // workgroup with.  Workgroup i serves head i % H (one XCD per head when H is
@@ -36,6 +49,18 @@ namespace {
 using namespace dev;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// LDS slot of V unit u = g * 16 + token (8 dims of dim group g of one
+// token): the token index is XOR-ed with 4 * (g % 4), so that the 16 lanes
+// of a transpose read, which take tokens t0 .. t0+3 (t0 % 4 == 0) of dim
+// groups g0 and g0 + 1 (and the next 16 lanes g0 + 2, g0 + 3), meet 16
+// distinct 16-byte slots of the LDS banks; writes of whole rows of 16
+// tokens stay conflict-free (a permutation inside a row).
+__device__ __forceinline__ int v_slot(int u) { return u ^ (4 * ((u >> 4) & 3)); }
+
+// Slack of the reference maximum, in log2 units: weights stay below 2^8
+// (exact in fp16's range; the fp32 sums have room to spare).
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ int rows_of(const PrefillArgs& a, int b) {
   return max(0, a.query_start[b + 1] - a.query_start[b]);
@@ -85,25 +110,36 @@ __device__ __forceinline__ int seq_of_group(const int* s_group, int B, int t) {
   return lo;
 }
 
+// Two waves per SIMD (two workgroups per CU): the register budget that
+// allows fits the kernel without spilling.
 template <int D>
-__global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillArgs a) {
-  constexpr int kK = D / 32;
-  constexpr int kS = D / 16;
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void pa_prefill_kernel(PrefillArgs a) {
+  typedef float f16x16 __attribute__((ext_vector_type(16)));
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef short s8v __attribute__((ext_vector_type(8)));
+  constexpr int kQK = D / 16;                           // score MFMAs (16 dims each)
+  constexpr int kSl = D / 32;                           // output slices of 32 dims
   constexpr int kTile = D * kBlockTokens * 2;           // bytes of one K (or V) tile
   constexpr int kTileUnits = kTile / 16;                // 16-byte units of one tile
-  constexpr int kUnits = 2 * kTileUnits / (64 * kPrefillWaves);   // per thread: K and V
+  constexpr int kThreads = 64 * kPrefillWaves;
+  constexpr int kLoaders = 2 * kTileUnits < kThreads ? 2 * kTileUnits : kThreads;
+  constexpr int kUnits = 2 * kTileUnits / kLoaders;     // 16-byte units per loading thread
   constexpr int R = kPrefillTiles;
-  static_assert(kUnits >= 1 && R == 4, "tile split; four stages, consumed in pairs");
+  constexpr int kStages = 4;
+  static_assert(kUnits >= 1 && R % kStages == 0 && kLoaders % kWave == 0,
+                "tile split; four stages consumed in pairs; whole loading waves");
   extern __shared__ int smem[];
   __shared__ int s_wave[kPrefillWaves];
-  __shared__ u4v s_kv[R][2 * kTileUnits];               // stage: K tile, then V tile
+  __shared__ u4v s_kv[kStages][2 * kTileUnits];         // stage: K tile, then V tile
   int* s_group = smem;                                  // B + 1
   int* s_ids = smem + a.B + 1;                          // block ids of the sequence
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int qc = lane % 16;
+  const int col = lane % 32;                            // query column of this lane
+  const int hf = lane / 32;                             // k-slot half of this lane
 
   group_prefix(a, s_group, s_wave);
   const int gt = blockIdx.x / a.H;
@@ -125,41 +161,54 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillA
   }
   __syncthreads();
 
-  // this lane's query row: wave w serves rows row0 + 16w ..
-  const int wrow = 16 * wave + qc;
+  // this lane's query row: wave w serves rows row0 + 32w ..; a wave with no
+  // row skips the arithmetic (it still loads, stages and meets the barriers)
+  const bool wave_rows = 32 * wave < grows;
+  const int wrow = 32 * wave + col;
   const int qrow = a.query_start[b] + row0 + wrow;
   const bool row_ok = wrow < grows && qrow >= 0 && qrow < a.num_rows;
   const int p_q = p_group + wrow;
-  const int tg = lane / 16;
   const rsrc_t qr = make_rsrc(a.q, (uint32_t)((size_t)a.num_rows * a.H * D * 2));
-  const uint32_t qoff = row_ok ? (uint32_t)((((size_t)qrow * a.H + h) * D + 8 * tg) * 2)
+  const uint32_t qoff = row_ok ? (uint32_t)((((size_t)qrow * a.H + h) * D + 8 * hf) * 2)
                                : 0xFFFFFFF0u;           // past the resource: reads 0
-  h8v qb[kK];
+  h8v qb[kQK];                                          // B operands: dims 16i + 8hf ..
 #pragma unroll
-  for (int i = 0; i < kK; ++i)
-    qb[i] = as_h8(__builtin_amdgcn_raw_buffer_load_b128(qr, qoff + (row_ok ? i * 64 : 0), 0, 0));
+  for (int i = 0; i < kQK; ++i)
+    qb[i] = as_h8(__builtin_amdgcn_raw_buffer_load_b128(qr, qoff + (row_ok ? i * 32 : 0), 0, 0));
   // keep the query loads ahead of the ring's first tiles (every step reads them)
   __builtin_amdgcn_sched_barrier(0);
-
-  float m = kNegInf, l = 0.0f;
-  f4v acc[kS];
+  // The scores are taken as (sign(scale) q) . k (an exact negation), so that
+  // their maximum is the maximum of the scaled scores; weights are then
+  // exp2(s * |scale log2 e| - m) with one fused multiply-add.
+  const float sabs = fabsf(a.scale_log2);
+  if (a.scale_log2 < 0.0f) {
 #pragma unroll
-  for (int s = 0; s < kS; ++s) acc[s] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
+  }
+  const int p_wave = p_group + 32 * wave;               // position of the wave's first row
+
+  float m = kNegInf, l = 0.0f;        // reference maximum (scaled, log2); sum over this lane's tokens
+  f16x16 acc[kSl];
+#pragma unroll
+  for (int s = 0; s < kSl; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
 
   if (nblk > 0) {
     const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
     const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
     const size_t block_stride = (size_t)a.H * kTile;
-    // The tile pair is 2 * kTileUnits 16-byte units, unit u = tid + 256 * k
-    // (K for u < kTileUnits, V after).  With two units per thread, unit 0 is
-    // K and unit 1 is V; with one, waves 0-1 take K and waves 2-3 take V:
-    // either way the choice is uniform per wave, so the buffer resource stays
-    // in scalar registers.
-    auto unit_is_v = [&](int k) { return kUnits == 2 ? k == 1 : wave >= kPrefillWaves / 2; };
+    // The tile pair is 2 * kTileUnits 16-byte units; the first kLoaders
+    // threads load them, unit u = tid + kLoaders * k (K for u < kTileUnits,
+    // V after).  kTileUnits and kLoaders are multiples of 64, so the choice
+    // of K or V is uniform per wave and the buffer resource stays in scalar
+    // registers.
+    const bool loader = wave * kWave < kLoaders;        // uniform per wave
+    auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
     const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
     auto fetch = [&](u4v (&r)[kUnits], int j) {
       const int jj = min(j, nblk - 1);
-      const uint32_t bytes = j < nblk ? kTile : 0u;
+      const uint32_t bytes = j < nblk && loader ? kTile : 0u;
       const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
 #pragma unroll
       for (int k = 0; k < kUnits; ++k)
@@ -168,40 +217,122 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillA
     };
     auto stage = [&](const u4v (&r)[kUnits], int st, int j) {
       const int valid = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
+      if (!loader) return;                              // uniform per wave
 #pragma unroll
       for (int k = 0; k < kUnits; ++k) {
         u4v w = r[k];
         // a V unit holds 8 dims of token (tid % kTileUnits) % 16
-        const bool zero = unit_is_v(k) && (tid % kTileUnits) % kBlockTokens >= valid;
+        const int u = tid % kTileUnits;
+        const bool is_v = unit_is_v(k);
+        const bool zero = is_v && u % kBlockTokens >= valid;
         w.x = zero ? 0u : w.x;
         w.y = zero ? 0u : w.y;
         w.z = zero ? 0u : w.z;
         w.w = zero ? 0u : w.w;
-        s_kv[st][(unit_is_v(k) ? kTileUnits : 0) + tid % kTileUnits] = w;
+        s_kv[st][is_v ? kTileUnits + v_slot(u) : u] = w;
       }
     };
-    // two tiles per step: j and j + 1 from stages sa and sa + 1
+    // transpose reads (offsets in halves inside a V tile): lane i = l%16 of
+    // its 16-lane group addresses dims 8*g + 4*(i%2) .. +3 of token
+    // 4hf + i/4 (lo) and of token 8 + 4hf + i/4 (hi), g = 2*(col/16) +
+    // (i%4)/2 (+ 4 per slice of 32 dims), at the swizzled slots
+    const int qi = lane % 16;
+    const int g0 = 2 * (col / 16) + (qi & 3) / 2;
+    const int tr_lo = v_slot(g0 * kBlockTokens + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
+    const int tr_hi = v_slot(g0 * kBlockTokens + 8 + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
+    // this lane's K row: token col of the pair (tile col / 16), dims 16i + 8hf ..
+    const int k_unit = (2 * 0 + hf) * kBlockTokens + col % 16;   // + 2i * 16 per MFMA
     auto compute = [&](int sa, int j) {
-      const int va = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
-      const int vb = j + 1 < nblk ? min(kBlockTokens, ctx - (j + 1) * kBlockTokens) : 0;
+      if (!wave_rows) return;                           // uniform per wave
       const int t0 = j * kBlockTokens;
-      u4v ka[kK], kb[kK];
+      const u4v* kt = s_kv[sa + col / 16];
+      u4v kr[kQK];                                      // A operands: token col of the pair
 #pragma unroll
-      for (int i = 0; i < kK; ++i) {
-        ka[i] = s_kv[sa][i * kWave + lane];
-        kb[i] = s_kv[sa + 1][i * kWave + lane];
+      for (int i = 0; i < kQK; ++i) kr[i] = kt[k_unit + 2 * i * kBlockTokens];
+      f16x16 sc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kQK; ++i)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(kr[i]), qb[i], sc, 0, 0, 0);
+      // register r: token tk = 8*(r/4) + 4*hf + r%4 of the pair (tile tk / 16).
+      // A pair wholly at or before the wave's first row (hence inside the
+      // context and visible to every row of the wave) needs no mask; the
+      // masked path gives the same result for the tokens it keeps.
+      const bool full = t0 + 2 * kBlockTokens - 1 <= p_wave;   // uniform per wave
+      bool live[16];
+      float mx = kNegInf;
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      } else {
+        const int va = j < nblk ? min(kBlockTokens, ctx - t0) : 0;
+        const int vb = j + 1 < nblk ? min(kBlockTokens, ctx - t0 - kBlockTokens) : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tk = 8 * (r / 4) + 4 * hf + r % 4;
+          live[r] = row_ok & (tk % kBlockTokens < (tk < kBlockTokens ? va : vb)) & (t0 + tk <= p_q);
+          mx = fmaxf(mx, live[r] ? sc[r] : kNegInf);
+        }
       }
-      mfma_update_pair<D>(
-          ka, kb, qb, a.scale_log2,
-          [&](int tok) { return row_ok && tok < va && t0 + tok <= p_q; },
-          [&](int tok) { return row_ok && tok < vb && t0 + kBlockTokens + tok <= p_q; },
-          m, l, acc, reinterpret_cast<const _Float16*>(&s_kv[sa][kTileUnits]),
-          reinterpret_cast<const _Float16*>(&s_kv[sa + 1][kTileUnits]), lane);
+      auto sw = __builtin_amdgcn_permlane32_swap(as_u32(mx), as_u32(mx), false, false);
+      mx = fmaxf(as_f32(sw[0]), as_f32(sw[1]));
+      // The reference maximum m moves only when the pair's maximum exceeds it
+      // by more than kRescaleSlack, so the weights stay below 2^kRescaleSlack
+      // and the accumulators are rescaled rarely.  Both lanes of a row take
+      // the same decision.
+      const float mxs = mx == kNegInf ? kNegInf : mx * sabs;
+      if (mxs > m + kRescaleSlack) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mxs);   // m = -inf: 0
+#pragma unroll
+        for (int s = 0; s < kSl; ++s) acc[s] = acc[s] * alpha;
+        l *= alpha;
+        m = mxs;
+      }
+      const float mref = m == kNegInf ? 0.0f : m;
+      h8v pb[2];
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pb[r / 8][r % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], sabs, -mref));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pb[r / 8][r % 8] =
+              (_Float16)__builtin_amdgcn_exp2f(live[r] ? fmaf(sc[r], sabs, -mref) : kNegInf);
+      }
+      // running sum of the rounded weights, two per instruction
+      typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+      const h2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const h2v two = {pb[kk][e], pb[kk][e + 1]};
+          l = __builtin_amdgcn_fdot2(two, ones, l, false);
+        }
+#pragma unroll
+      for (int s = 0; s < kSl; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const _Float16* vt = reinterpret_cast<const _Float16*>(&s_kv[sa + kk][kTileUnits]);
+          const int off = s * 4 * kBlockTokens * 8;       // 4 dim groups per slice
+          const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s4v*)(vt + off + tr_lo));
+          const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s4v*)(vt + off + tr_hi));
+          const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, both), pb[kk],
+                                                          acc[s], 0, 0, 0);
+        }
+      }
     };
-    // R tiles in flight, four LDS stages: tiles j0 .. j0+3 of a round go to
-    // stages 0 .. 3, a barrier after each pair, then the pair is consumed.
-    // Steps past the last block see valid = 0 (exact no-ops), so the loop
-    // runs whole rounds with no exit in its body.
+    // R tiles in flight in registers, four LDS stages: tile j + r of a
+    // round goes to stage r % 4, a barrier after each pair, then the pair is
+    // consumed.  A stage is rewritten only after the barrier that follows
+    // the last use of its previous tile.  Steps past the last block see
+    // valid = 0 (exact no-ops), so the loop runs whole rounds with no exit
+    // in its body.
     u4v ring[R][kUnits];
 #pragma unroll
     for (int r = 0; r + 1 < R; ++r) fetch(ring[r], r);
@@ -209,27 +340,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void pa_prefill_kernel(PrefillA
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         fetch(ring[(r + R - 1) % R], j + r + R - 1);
-        stage(ring[r], r, j + r);
+        stage(ring[r], r % kStages, j + r);
         if (r % 2 == 1) {
           __syncthreads();
-          compute(r - 1, j + r - 1);
+          compute((r - 1) % kStages, j + r - 1);
         }
       }
     }
   }
 
-  // rows at a negative position (more queries than cached tokens) are zero
-  l = cross_row_sum(l);
+  // rows at a negative position (more queries than cached tokens) are zero;
+  // lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row
+  auto sw = __builtin_amdgcn_permlane32_swap(as_u32(l), as_u32(l), false, false);
+  l = as_f32(sw[0]) + as_f32(sw[1]);
   if (row_ok) {
     const float inv = p_q >= 0 && l > 0.0f ? 1.0f / l : 0.0f;
-    _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * tg;
+    _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * hf;
 #pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      h4v o;
+    for (int s = 0; s < kSl; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][r] * inv);
-      *reinterpret_cast<h4v*>(orow + 16 * s) = o;
-    }
+      for (int q = 0; q < 4; ++q) {
+        h4v o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][4 * q + r] * inv);
+        *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
+      }
   }
 }
 

@@ -64,6 +64,24 @@ def test_ragged_prompts_and_chunks(H, D):
     assert zero.sum() == 3 and not to_host(out)[zero].any()
 
 
+@pytest.mark.parametrize("mult", [1.0, -1.0, 0.0, 4.0])
+def test_scale_sign_zero_and_rising_scores(mult):
+    """Keys that grow along the sequence (scores rise, so the online
+    softmax's reference maximum is raised many times), with the scale
+    D^-1/2 times 1, -1 (the scores' minimum decides), 0 (a plain average of
+    the visible values) and 4 (sharp weights)."""
+    H, D = 4, 128
+    lens = [300, 64, 17]
+    q, kp, vp, tables, lens, qs = _ragged(70, H, D, lens, [300, 10, 17])
+    for b, n in enumerate(lens):
+        for t in range(int(n)):
+            kp[tables[b, t // 16], :, :, t % 16, :] *= np.float16(1.0 + t / 40.0)
+    scale = float(np.float32(mult * D ** -0.5))
+    out = run_prefill(q, to_dev(kp), to_dev(vp), tables, lens, qs, scale, 300)
+    ref = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
+    assert_close(out, ref, f"prefill, scale {mult} / sqrt(D), rising keys")
+
+
 def test_two_chunks_equal_one_pass_bitwise():
     """Each query column's arithmetic is independent of the others, and the
     blocks a tile streams past a row's position are exact no-ops for it: a

@@ -157,14 +157,22 @@ def prefill_asm(tmp_path_factory):
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D):
-    body = kernel_body(prefill_asm, f"pa_prefill_kernelILi{D}ELi0E")
+    """The prefill's tile loop: 32x32x16 MFMAs, the K/V buffer resources stay
+    scalar (no waterfall loop around a load), and three tiles stay in flight
+    (D/64 16-byte loads per thread and tile) at every wait."""
+    name = f"pa_prefill_kernelILi{D}E"
+    body = kernel_body(prefill_asm, name)
     rings = [t for t in tile_loops(body).values() if "v_mfma" in t]
     assert len(rings) == 1, "expected one MFMA tile loop"
-    assert "vmcnt(0)" not in rings[0]
-    waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", rings[0])]
-    assert waits and min(waits) >= 2 * (D // 32)
-    assert meta(prefill_asm, f"pa_prefill_kernelILi{D}E", "vgpr_spill_count") == 0
-    assert meta(prefill_asm, f"pa_prefill_kernelILi{D}E", "vgpr_count") <= 256
+    ring = rings[0]
+    assert "v_mfma_f32_32x32x16_f16" in ring
+    assert "s_cbranch_execnz" not in ring
+    assert "vmcnt(0)" not in ring
+    waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", ring)]
+    assert waits and min(waits) >= 3 * (D // 64)
+    assert meta(prefill_asm, name, "vgpr_spill_count") == 0
+    assert meta(prefill_asm, name, "private_segment_fixed_size") == 0
+    assert meta(prefill_asm, name, "vgpr_count") <= 256
 
 
 @pytest.mark.parametrize("D", [128, 64])
