@@ -55,6 +55,9 @@ def parse():
                     help="write the HBM-traffic record from two rocprofv3 counter_collection "
                          "CSVs (FETCH_SIZE pass, WRITE_SIZE pass; both runs with --copy-probe) "
                          "and exit; needs no GPU")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="batch workloads: kv_append then pa_decode (two launches) instead of "
+                         "the fused pa_decode_append")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the HBM read probes (achievable-bandwidth references)")
     return ap.parse_args()
@@ -107,7 +110,7 @@ def kernel_source_sha256():
     describe the code that runs."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("api.hip", "pa_common.h", "pa_decode.hip", "pa_decode_flat.hip"):
+    for name in ("api.hip", "kernels.h", "pa_common.h", "pa_decode.hip", "pa_decode_flat.hip"):
         rel = os.path.join("paged_kv_cache_03_amd", "csrc", name)
         h.update(rel.encode())
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -141,7 +144,7 @@ def counter_kib_by_kernel(path, counter):
     return vals
 
 
-def write_traffic_record(fetch_csv, write_csv, workload="batch200_append_seed2"):
+def write_traffic_record(fetch_csv, write_csv, workload="batch200_seed2_pa_decode_append"):
     """HBM bytes per pa_decode call (decode + merge kernels) from the two
     counter passes, each scaled by what the same counter reads for the 1 GiB
     device copy of --copy-probe (bytes moved / counter bytes), stored with the
@@ -219,7 +222,8 @@ class Run:
 
 def setup_batch(torch, dev, wl, args, batch, seed):
     """One layer; each step appends one token per sequence and decodes."""
-    from paged_kv_cache_03_amd import default_partition, kv_append, pa_decode, pa_decode_workspace_size
+    from paged_kv_cache_03_amd import (default_partition, kv_append, pa_decode, pa_decode_append,
+                                       pa_decode_workspace_size)
     case = wl.gpt_batch(batch, seed=seed, append=True, fill=False)
     B, H, D = case.batch, case.num_heads, case.head_dim
     kp = wl.device_pool(torch, case, 0, 0, dev)
@@ -234,22 +238,36 @@ def setup_batch(torch, dev, wl, args, batch, seed):
     ws = torch.empty(max(1, pa_decode_workspace_size(B, H, D, max_ctx, part)), dtype=torch.uint8,
                      device=dev)
     kv_bytes, algo_bytes = algorithmic_bytes(case.context_lens, H, D)
+    fused = strategy == "flat" and not args.separate_append
 
-    def step(events):
-        kv_append(k_new, v_new, slots, kp, vp)
-        events.append(torch.cuda.Event(enable_timing=True))
-        events[-1].record()
-        pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
-                  workspace=ws, partition_tokens=part)
-        events.append(torch.cuda.Event(enable_timing=True))
-        events[-1].record()
+    if fused:
+        # the call also reads the new K/V rows and writes them to the pools
+        algo_bytes += 2 * (2 * B * H * D * 2)
 
+        def step(events):
+            events.append(torch.cuda.Event(enable_timing=True))
+            events[-1].record()
+            pa_decode_append(q, k_new, v_new, kp, vp, tables, lens, case.scale, out,
+                             max_context_len=max_ctx, workspace=ws)
+            events.append(torch.cuda.Event(enable_timing=True))
+            events[-1].record()
+    else:
+        def step(events):
+            kv_append(k_new, v_new, slots, kp, vp)
+            events.append(torch.cuda.Event(enable_timing=True))
+            events[-1].record()
+            pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=max_ctx,
+                      workspace=ws, partition_tokens=part)
+            events.append(torch.cuda.Event(enable_timing=True))
+            events[-1].record()
+
+    how = ("kv_append of 1 token/sequence fused into pa_decode (pa_decode_append) per step"
+           if fused else "kv_append of 1 token/sequence + pa_decode per step")
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
-               algo_bytes=algo_bytes, strategy=strategy, part=part, extra={},
+               algo_bytes=algo_bytes, strategy=strategy, part=part, extra={}, fused=fused,
                config={"workload": f"one layer, batch {B}, 32 heads x 128 dims fp16, 16-token "
                                    "blocks, contexts prompt U[32,256] + geometric(mean 500) "
-                                   "capped at 2048, kv_append of 1 token/sequence + pa_decode "
-                                   "per step",
+                                   f"capped at 2048, {how}",
                        "batch": B, "heads": H, "head_dim": D, "block_tokens": 16,
                        "context_tokens": case.kv_tokens(), "max_context": max_ctx,
                        "num_blocks": case.num_blocks, "strategy": strategy,
@@ -617,7 +635,7 @@ def main():
     kv_per_call = run.kv_bytes / (len(dec_ms) / args.steps)
     dec_gbs = kv_per_call / dec_avg_s / 1e9
     achieved = run.algo_bytes / dec_avg_s / 1e9
-    headline = args.workload == "batch200" and run.strategy == "flat"
+    headline = args.workload == "batch200" and getattr(run, "fused", False)
     result = {
         "metric": "pa_decode K/V GB/s (% MI355X HBM peak) + seq-layers/s at batch 200",
         "value": round(step_gbs, 2),
@@ -638,7 +656,9 @@ def main():
         "pa_decode_kv_gbs": round(dec_gbs, 2),
         "pa_decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
-            "kernel": "pa_decode (decode + merge kernels, one call)",
+            "kernel": ("pa_decode_append (fused append + decode kernel, merge kernel; one call)"
+                       if getattr(run, "fused", False) else
+                       "pa_decode (decode + merge kernels, one call)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

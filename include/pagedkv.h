@@ -137,6 +137,39 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
                      void* workspace, size_t workspace_bytes,
                      int32_t partition_tokens, uint32_t flags, void* stream);
 
+/*
+ * One decode step with its append fused in: for every sequence b with
+ * context_lens[b] >= 1, the keys and values of its new token, k_new[b] and
+ * v_new[b] ([B][H][D] fp16), are written to its last position,
+ * t = context_lens[b] - 1 (block block_tables[b][t/16], slot t%16 of
+ * k_pool / v_pool), and the decode of pkv_pa_decode over positions
+ * 0 .. t follows, the new token included ("PagedAttention",
+ * e-fortepiano.pl, "Descripció": the key and value of each generated token
+ * go to the sequence's last block before the next attention step).  The
+ * pools and the output are those of pkv_kv_append with slot
+ * block_tables[b][t/16] * 16 + t%16 for each b, then pkv_pa_decode, bit for
+ * bit.  The decode kernel takes the new token into the tile it holds in
+ * registers where the sequence's last block is read, and the merge kernel
+ * of the same call writes it to the pools, so the append costs no launch of
+ * its own and no wait inside the decode's load stream.
+ *
+ * device: q, k_new, v_new, k_pool, v_pool (written), out (16-byte aligned),
+ *         block_tables, context_lens, workspace (as for pkv_pa_decode, size
+ *         pkv_pa_decode_workspace_size).  The last block of each sequence
+ *         must not be shared with another sequence of the batch (a shared
+ *         block is copied before it is written, see pkv_cow_copy_blocks).
+ * host:   as for pkv_pa_decode; flags 0 or PKV_DECODE_KEEP_KV_CACHED.
+ *         Always the flat strategy: a shape it cannot stage returns
+ *         PKV_ERR_UNSUPPORTED (use pkv_kv_append + pkv_pa_decode_ex then).
+ */
+int pkv_pa_decode_append(const void* q, const void* k_new, const void* v_new,
+                         void* k_pool, void* v_pool, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t max_context_len, int32_t B, int32_t H, int32_t D,
+                         int32_t block_size, int32_t num_blocks, float scale,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, void* stream);
+
 size_t pkv_pa_decode_workspace_size_ex(int32_t B, int32_t H, int32_t D,
                                        int32_t max_context_len,
                                        int32_t partition_tokens);

@@ -53,6 +53,9 @@ SIGNATURES = {
     "pkv_vkv_capacity": (_vp, [_vp]),
     "pkv_vkv_append": (_c.c_int, [_vp, _i32, _vp, _vp, _i32p, _i32p, _i32, _vp]),
     "pkv_vkv_stats": (_c.c_int, [_vp, _vp]),
+    "pkv_pa_decode_append": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _i32p, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _c.c_float, _vp, _vp,
+                                         _c.c_size_t, _c.c_uint32, _vp]),
     "pkv_kv_append": (_c.c_int, [_vp, _vp, _i32p, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pkv_cow_copy_blocks": (_c.c_int, [_c.POINTER(_vp), _c.POINTER(_vp), _i32, _i32p, _i32, _i32,
                                        _c.c_int64, _vp]),

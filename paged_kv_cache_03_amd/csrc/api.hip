@@ -165,12 +165,17 @@ size_t pkv_pa_decode_workspace_size(int32_t B, int32_t H, int32_t D, int32_t max
   return pkv_pa_decode_workspace_size_ex(B, H, D, max_context_len, 0);
 }
 
-int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
-                     int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
-                     void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                     uint32_t flags, void* stream) {
+namespace {
+
+// pkv_pa_decode_ex, and with k_new / v_new the decode with the fused append
+// (flat strategy only).
+int decode_impl(const void* q, const void* k_pool, const void* v_pool,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
+                int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                uint32_t flags, const void* k_new, const void* v_new, void* stream) {
+  const bool append = k_new != nullptr || v_new != nullptr;
   if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
   if (flags & ~(uint32_t)PKV_DECODE_KEEP_KV_CACHED) return PKV_ERR_BAD_SHAPE;
   const bool keep_cached = (flags & PKV_DECODE_KEEP_KV_CACHED) != 0;
@@ -181,11 +186,14 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
       (long long)max_blocks_per_seq * kBlockTokens < max_context_len)
     return PKV_ERR_BAD_SHAPE;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PKV_ERR_NULL_PTR;
+  if (append && (!k_new || !v_new)) return PKV_ERR_NULL_PTR;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PKV_ERR_MISALIGNED;
+  if (append && (!aligned(k_new, 16) || !aligned(v_new, 16))) return PKV_ERR_MISALIGNED;
 
   const Plan plan = make_plan(B, H, D, max_context_len, partition_tokens);
+  if (append && !plan.flat) return PKV_ERR_UNSUPPORTED;
   if (plan.total > 0) {
     if (!workspace) return PKV_ERR_NULL_PTR;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_MISALIGNED;
@@ -222,6 +230,8 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
     a.contig = false;
     a.row_tokens = 0;
     a.capacity = nullptr;
+    a.k_new = static_cast<const _Float16*>(k_new);
+    a.v_new = static_cast<const _Float16*>(v_new);
     e = pkv::launch_pa_decode_flat(a, D, fw * 64, static_cast<hipStream_t>(stream));
   } else {
     const long long grid = (long long)B * (H / wpg) * (plan.max_parts > 0 ? plan.max_parts : 1);
@@ -249,6 +259,31 @@ int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
     e = pkv::launch_pa_decode(a, D, (int)grid, wpg * 64, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+int pkv_pa_decode_ex(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
+                     int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                     uint32_t flags, void* stream) {
+  return decode_impl(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
+                     workspace_bytes, partition_tokens, flags, nullptr, nullptr, stream);
+}
+
+int pkv_pa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                         void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                         int32_t H, int32_t D, int32_t block_size, int32_t num_blocks, float scale,
+                         void* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                         void* stream) {
+  if (!k_new || !v_new) return PKV_ERR_NULL_PTR;
+  return decode_impl(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
+                     workspace_bytes, 0, flags, k_new, v_new, stream);
 }
 
 int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -312,6 +347,8 @@ int pkv_contig_decode(const void* q, const void* k_buf, const void* v_buf, int32
   a.contig = true;
   a.row_tokens = row_tokens;
   a.capacity = capacity;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   const hipError_t e = pkv::launch_pa_decode_flat(a, D, fw * 64, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

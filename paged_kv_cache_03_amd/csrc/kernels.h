@@ -93,6 +93,11 @@ struct FlatArgs {
   bool contig;
   int row_tokens;
   const int32_t* capacity;   // contiguous: tokens each sequence may read (or null)
+  // Append fused into the decode (or null): [B][H][D] keys / values of each
+  // sequence's new token, written to its last position (context_lens[b] - 1)
+  // in the pools before that position is read.
+  const _Float16* k_new;
+  const _Float16* v_new;
 };
 
 // Grouped decode (pa_decode_grouped.hip): groups of up to kGroupMaxMembers

@@ -106,13 +106,18 @@ __device__ __forceinline__ uint32_t load_q_dword(const _Float16* q, size_t row,
   return __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(q + row * D, D * 2), lane_off4, 0, 0);
 }
 
-// Spread a query row held one dword per lane into this lane's groups
-// 4*i + row (16 bytes each), through the wave's own 256-byte LDS slot: the
-// wave's LDS operations run in order, so no barrier is needed.
+// Spread a row held one dword per lane into this lane's groups 4*i + row
+// (16 bytes each), through the wave's own 256-byte LDS slot.  The wave's LDS
+// operations run in order, so no barrier is needed; the wavefront-scope
+// fences (no instruction) tell the compiler that lanes read what other lanes
+// wrote, so it neither moves the reads past the writes nor reuses a lane's
+// earlier read of the slot (lanes at or past D/2 write nothing).
 template <int D>
 __device__ __forceinline__ void distribute_q(u4v (&q)[Geometry<D>::kLoads], uint32_t qn, int row,
                                              int lane, uint32_t* slot) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   if (lane < D / 2) slot[lane] = qn;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const u4v* rows = reinterpret_cast<const u4v*>(slot);
 #pragma unroll
   for (int i = 0; i < Geometry<D>::kLoads; ++i) q[i] = rows[4 * i + row];
@@ -142,8 +147,9 @@ __device__ __forceinline__ void store_acc(rsrc_t r, uint32_t off, const float (&
   }
 }
 
-template <int D, int kPolicy, bool kContig>
+template <int D, int kPolicy, bool kContig, bool kAppend>
 __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(FlatArgs a) {
+  static_assert(!(kContig && kAppend), "the append is for the block pool");
   constexpr int kAcc = Geometry<D>::kAcc;
   constexpr int kTile = Geometry<D>::kTileBytes;
   constexpr int kOut = Geometry<D>::kOutPerLane;
@@ -233,13 +239,43 @@ __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(Flat
   const uint32_t out_off = d0 * 2u;
   const uint32_t acc_off = d0 * 4u;
 
+  // With the append: the new token of the current segment's sequence (its
+  // last position, token tail - 1 of its last block), one dword per lane
+  // like the query, loaded when the segment opens if the segment ends the
+  // sequence.  At the last block it replaces the tile's slot in registers;
+  // the merge kernel writes it to the pools after this kernel.
+  uint32_t knew = 0, vnew = 0;
+  auto load_new = [&]() {
+    if constexpr (kAppend) {
+      const uint32_t bytes = seg_hi == seq_hi ? D * 2u : 0u;
+      const size_t nrow = ((size_t)b * a.H + h) * D;
+      knew = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.k_new + nrow, bytes), lane_off4, 0, 0);
+      vnew = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.v_new + nrow, bytes), lane_off4, 0, 0);
+    }
+  };
+  load_new();
 
   float m = kNegInf, l = 0.0f;
   float acc[kAcc];
 #pragma unroll
   for (int j = 0; j < kAcc; ++j) acc[j] = 0.0f;
 
-  auto step = [&](const Tile<D>& t, int s) {
+  auto step = [&](Tile<D>& t, int s) {
+    if constexpr (kAppend) {
+      if (s == seq_hi - 1) {           // uniform: the sequence's last block
+        // the new rows in the tile's lane layout (load i of lane l: dims
+        // 8 * (l / 16 + 4 i) .. +7), through the wave's query slot
+        u4v kn[Geometry<D>::kLoads], vn[Geometry<D>::kLoads];
+        distribute_q<D>(kn, knew, row, lane, s_q[wave]);
+        distribute_q<D>(vn, vnew, row, lane, s_q[wave]);
+        const bool mine = token == tail - 1;
+#pragma unroll
+        for (int i = 0; i < Geometry<D>::kLoads; ++i) {
+          t.k[i] = mine ? kn[i] : t.k[i];
+          t.v[i] = mine ? vn[i] : t.v[i];
+        }
+      }
+    }
     // one code path for every block: only a sequence's last block can be
     // partially filled, the others pass valid = 16
     consume<D, true>(t, q, a.scale_log2, token, s == seq_hi - 1 ? tail : kBlockTokens, m, l, acc);
@@ -271,6 +307,7 @@ __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(Flat
         b_next = seq_of(s_start, a.B, seg_hi);
         qn = load_q_dword<D>(a.q, (size_t)b_next * a.H + h, lane_off4);
       }
+      load_new();                      // (after the query loads: no load drain in the loop)
       m = kNegInf;
       l = 0.0f;
 #pragma unroll
@@ -297,10 +334,11 @@ __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(Flat
 done:;
 }
 
-// One wave per (sequence, head), four per workgroup.  Zero row for an empty
-// sequence; for a sequence cut across ranges, merge its pieces (weights
-// exp2(m_r - M)) in ascending range order; otherwise nothing (the decode
-// kernel wrote the row).  Sequence offsets come from the decode kernel
+// One wave per (sequence, head), four per workgroup.  With the fused
+// append, first write the sequence's new token to the pools.  Zero row for
+// an empty sequence; for a sequence cut across ranges, merge its pieces
+// (weights exp2(m_r - M)) in ascending range order; otherwise nothing (the
+// decode kernel wrote the row).  Sequence offsets come from the decode kernel
 // (ws_seq), so no prefix sum is redone here.
 template <int D>
 __global__ __launch_bounds__(256) void pa_decode_flat_merge_kernel(FlatArgs a) {
@@ -314,6 +352,22 @@ __global__ __launch_bounds__(256) void pa_decode_flat_merge_kernel(FlatArgs a) {
   const int S = a.ws_seq[b];
   const int E = a.ws_seq[b + 1];
   _Float16* orow = a.out + (size_t)bh * D;
+  if (a.k_new != nullptr && E > S) {
+    // the fused append: the new token (already used by the decode kernel)
+    // goes to the sequence's last position, slot tail - 1 of its last block;
+    // lanes 0 .. D/8-1 write K, the next D/8 lanes V, 16 bytes each
+    const int ctx = clamp_ctx(a.context_lens[b], a.ctx_limit);
+    const int t = ctx - 1;
+    const int id = a.block_tables[(size_t)b * a.max_blocks + t / kBlockTokens];
+    const size_t blk = (size_t)min(max(id, 0), a.num_blocks - 1);
+    const int g = lane % (D / 8);
+    if (lane < 2 * (D / 8)) {
+      const bool is_v = lane >= D / 8;
+      const u4v* src = reinterpret_cast<const u4v*>((is_v ? a.v_new : a.k_new) + (size_t)bh * D);
+      u4v* dst = reinterpret_cast<u4v*>(const_cast<void*>(is_v ? a.v_pool : a.k_pool));
+      dst[((blk * a.H + h) * (D / 8) + g) * kBlockTokens + t % kBlockTokens] = src[g];
+    }
+  }
   if (E == S) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) orow[lane * kPer + k] = (_Float16)0.0f;
@@ -355,20 +409,32 @@ size_t flat_lds_bytes(int B, int max_chunk) {
 hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream) {
   const size_t lds = flat_lds_bytes(a.B, a.max_chunk);
   const int grid = a.head_groups * a.nr;
+  const bool append = a.k_new != nullptr;
+#define PKV_FLAT_LAUNCH(DD, POL, CONTIG, APPEND)                                              \
+  hipLaunchKernelGGL((pa_decode_flat_kernel<DD, POL, CONTIG, APPEND>), dim3(grid), dim3(threads), \
+                     lds, stream, a)
+  const int pol = a.keep_cached ? kCachedPolicy : kStreamPolicy;
   if (a.contig) {
-    if (D == 128)
-      hipLaunchKernelGGL((pa_decode_flat_kernel<128, kStreamPolicy, true>), dim3(grid), dim3(threads), lds, stream, a);
-    else
-      hipLaunchKernelGGL((pa_decode_flat_kernel<64, kStreamPolicy, true>), dim3(grid), dim3(threads), lds, stream, a);
-  } else if (D == 128 && !a.keep_cached) {
-    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kStreamPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+    if (D == 128) PKV_FLAT_LAUNCH(128, kStreamPolicy, true, false);
+    else PKV_FLAT_LAUNCH(64, kStreamPolicy, true, false);
   } else if (D == 128) {
-    hipLaunchKernelGGL((pa_decode_flat_kernel<128, kCachedPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
-  } else if (!a.keep_cached) {
-    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kStreamPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+    if (pol == kStreamPolicy) {
+      if (append) PKV_FLAT_LAUNCH(128, kStreamPolicy, false, true);
+      else PKV_FLAT_LAUNCH(128, kStreamPolicy, false, false);
+    } else {
+      if (append) PKV_FLAT_LAUNCH(128, kCachedPolicy, false, true);
+      else PKV_FLAT_LAUNCH(128, kCachedPolicy, false, false);
+    }
   } else {
-    hipLaunchKernelGGL((pa_decode_flat_kernel<64, kCachedPolicy, false>), dim3(grid), dim3(threads), lds, stream, a);
+    if (pol == kStreamPolicy) {
+      if (append) PKV_FLAT_LAUNCH(64, kStreamPolicy, false, true);
+      else PKV_FLAT_LAUNCH(64, kStreamPolicy, false, false);
+    } else {
+      if (append) PKV_FLAT_LAUNCH(64, kCachedPolicy, false, true);
+      else PKV_FLAT_LAUNCH(64, kCachedPolicy, false, false);
+    }
   }
+#undef PKV_FLAT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int merge_grid = (a.B * a.H + 3) / 4;

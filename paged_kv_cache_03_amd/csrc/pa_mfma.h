@@ -177,7 +177,9 @@ __device__ __forceinline__ void mfma_update_pair(const u4v (&ka)[D / 32], const 
 // data and must not be live; their V rows are zeroed before use (they may
 // hold anything, NaN included, and weight 0 * NaN would still be NaN).
 // sv / svh: the wave's own LDS area of D * 16 fp16 (the wave's LDS
-// operations run in order, so no barrier is needed).
+// operations run in order, so no barrier is needed; the wavefront-scope
+// fences, which emit no instruction, keep the compiler from moving the
+// transpose reads, which take other lanes' data, across the writes).
 template <int D, typename Live>
 __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D / 32],
                                             float scale_log2, int valid, Live live, float& m,
@@ -186,6 +188,7 @@ __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D
   h4v pb;
   const float alpha = mfma_scores<D>(t.k, qb, scale_log2, live, m, l, pb, lane);
   const bool tok_ok = lane % 16 < valid;     // this lane's loaded token is l % 16
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     u4v w = t.v[i];
@@ -195,6 +198,7 @@ __device__ __forceinline__ void mfma_update(const MTile<D>& t, const h8v (&qb)[D
     w.w = tok_ok ? w.w : 0u;
     sv[i * kWave + lane] = w;
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   mfma_pv<D>(acc, alpha, pb, svh, lane);
 }
 

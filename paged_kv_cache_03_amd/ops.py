@@ -111,6 +111,53 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
     return out
 
 
+def pa_decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                     out=None, *, max_context_len=None, workspace=None, keep_cached=False):
+    """One decode step with its append fused in (one launch): the new token
+    of every non-empty sequence b (k_new[b], v_new[b]: [B][H][D] fp16) is
+    written to its last position context_lens[b] - 1 in the pools, then
+    ``pa_decode`` runs over the context, the new token included.  Same pools
+    and output, bit for bit, as ``kv_append`` with those slots followed by
+    ``pa_decode``.  The other arguments are those of ``pa_decode``."""
+    lib = _lib.load_library()
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    B, H, D = q.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, torch.float16, dev, ndim=3)
+        if tuple(t.shape) != (B, H, D):
+            raise ValueError(f"{name} must be [B][H][D] like q")
+    NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
+    if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
+        raise ValueError("k_pool and v_pool differ in size")
+    _need(block_tables, "block_tables", torch.int32, dev, ndim=2)
+    _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens do not match the batch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, dev, ndim=3)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B][H][D]")
+    need = pa_decode_workspace_size(B, H, D, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+        ws_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        code = lib.pkv_pa_decode_append(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), max_context_len, B, H, D, BLOCK_TOKENS, NB,
+            float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+            _lib.DECODE_KEEP_KV_CACHED if keep_cached else 0, _stream_handle(dev))
+    _lib.check("pkv_pa_decode_append", code)
+    return out
+
+
 def pa_decode_grouped_workspace_size(batch, num_heads, head_dim, max_context_len, num_groups,
                                      group_size=16):
     return int(_lib.load_library().pkv_pa_decode_grouped_workspace_size(

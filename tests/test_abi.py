@@ -94,6 +94,42 @@ def test_plain_decode_entry_checks_too(lib):
                              A16, 1 << 30, None) == _lib.ERR_UNSUPPORTED
 
 
+def decode_append(lib, **kw):
+    args = dict(q=A16, kn=A16, vn=A16, k=A16, v=A16, tables=A16, maxb=128, ctx=A16, maxctx=2048,
+                B=4, H=32, D=128, bs=16, nb=1024, scale=0.088, out=A16, ws=A16, wsb=1 << 30,
+                flags=0)
+    args.update(kw)
+    return lib.pkv_pa_decode_append(args["q"], args["kn"], args["vn"], args["k"], args["v"],
+                                    args["tables"], args["maxb"], args["ctx"], args["maxctx"],
+                                    args["B"], args["H"], args["D"], args["bs"], args["nb"],
+                                    args["scale"], args["out"], args["ws"], args["wsb"],
+                                    args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=8), _lib.ERR_UNSUPPORTED),
+    (dict(D=96), _lib.ERR_BAD_SHAPE),
+    (dict(maxb=127), _lib.ERR_BAD_SHAPE),
+    (dict(flags=2), _lib.ERR_BAD_SHAPE),
+    (dict(kn=None), _lib.ERR_NULL_PTR),
+    (dict(vn=None), _lib.ERR_NULL_PTR),
+    (dict(kn=None, B=0), _lib.ERR_NULL_PTR),       # the new rows are always required
+    (dict(q=None), _lib.ERR_NULL_PTR),
+    (dict(kn=A4), _lib.ERR_MISALIGNED),
+    (dict(vn=A4), _lib.ERR_MISALIGNED),
+    (dict(ws=None), _lib.ERR_NULL_PTR),
+    (dict(wsb=64), _lib.ERR_WORKSPACE_TOO_SMALL),
+    (dict(B=5000, maxctx=1 << 16, maxb=4096), _lib.ERR_UNSUPPORTED),   # flat staging too big
+])
+def test_decode_append_rejects_bad_arguments(lib, kw, code):
+    assert decode_append(lib, **kw) == code
+
+
+def test_decode_append_empty_batch_is_a_no_op(lib):
+    assert decode_append(lib, B=0, q=None, k=None, v=None, tables=None, ctx=None,
+                         out=None) == _lib.OK
+
+
 def test_workspace_size(lib):
     B, H, D, ctx = 200, 32, 128, 2048
     # default plan: the flat strategy, whose partial pieces do not grow with

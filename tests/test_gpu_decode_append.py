@@ -1,0 +1,133 @@
+"""The decode step with its append fused in (pkv_pa_decode_append), on the
+GPU through the C ABI.
+
+The fused call must leave the pools and produce the output of kv_append
+(each sequence's new token at its last position) followed by pa_decode, bit
+for bit, and match the float64 oracle (append, then decode) within max-abs
+2e-3 and relative L2 1e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import append_ref, paged_decode_ref
+from paged_kv_cache_03_amd import kv_append, pa_decode, pa_decode_append
+from tests._gpu import assert_close, device_pools, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16)
+
+
+def _last_slots(tables, lens):
+    return np.array([tables[b, (n - 1) // 16] * 16 + (n - 1) % 16 if n > 0 else -1
+                     for b, n in enumerate(lens)], dtype=np.int32)
+
+
+def _both_ways(q, k_new, v_new, kp, vp, tables, lens, scale, max_ctx, keep_cached=False):
+    """(pools, out) of kv_append + pa_decode and of the fused call, each on
+    its own copy of the pools."""
+    slots = _last_slots(tables, lens)
+    kp1, vp1 = kp.clone(), vp.clone()
+    print(f"separate: B={len(lens)} max_ctx={max_ctx}", flush=True)
+    kv_append(to_dev(k_new), to_dev(v_new), to_dev(slots), kp1, vp1)
+    out1 = pa_decode(to_dev(q), kp1, vp1, to_dev(tables), to_dev(lens), scale,
+                     max_context_len=max_ctx, keep_cached=keep_cached)
+    kp2, vp2 = kp.clone(), vp.clone()
+    print(f"fused: B={len(lens)} max_ctx={max_ctx}", flush=True)
+    out2 = pa_decode_append(to_dev(q), to_dev(k_new), to_dev(v_new), kp2, vp2, to_dev(tables),
+                            to_dev(lens), scale, max_context_len=max_ctx, keep_cached=keep_cached)
+    torch.cuda.synchronize()
+    return (kp1, vp1, out1), (kp2, vp2, out2), slots
+
+
+def _ragged(seed, H, D, lens):
+    rng = np.random.default_rng(seed)
+    nblk = [-(-n // 16) for n in lens]
+    NB = sum(nblk) + 5
+    ids = rng.permutation(NB).astype(np.int32)
+    tables = np.full((len(lens), max(max(nblk), 1)), -1, dtype=np.int32)
+    p = 0
+    for b, nb in enumerate(nblk):
+        tables[b, :nb] = ids[p:p + nb]
+        p += nb
+    kp = wl.normal_fp16(rng, wl.pool_shape(NB, H, D))
+    vp = wl.normal_fp16(rng, wl.pool_shape(NB, H, D))
+    for row, n in zip(tables, lens):          # the new token's slot and those after it: NaN
+        if n > 0:
+            blk = row[(n - 1) // 16]
+            kp[blk, :, :, (n - 1) % 16:, :] = np.nan
+            vp[blk, :, :, (n - 1) % 16:, :] = np.nan
+    q = wl.normal_fp16(rng, (len(lens), H, D))
+    k_new = wl.normal_fp16(rng, (len(lens), H, D))
+    v_new = wl.normal_fp16(rng, (len(lens), H, D))
+    return q, k_new, v_new, kp, vp, tables, np.array(lens, dtype=np.int32)
+
+
+@pytest.mark.parametrize("H,D,keep", [(4, 64, False), (6, 128, False), (32, 128, False),
+                                      (32, 128, True)])
+def test_ragged_fused_equals_separate(H, D, keep):
+    """Empty sequences, a one-token context (the new token alone), new
+    tokens at every slot offset, a new token opening a block, and contexts
+    long enough that ranges cut sequences."""
+    lens = [0, 1, 16, 17, 32, 33, 100, 15, 2047, 0, 700, 48, 1, 513, 1300, 64]
+    q, k_new, v_new, kp, vp, tables, lens = _ragged(90 + H + D, H, D, lens)
+    scale = float(np.float32(D ** -0.5))
+    (kp1, vp1, out1), (kp2, vp2, out2), slots = _both_ways(
+        q, k_new, v_new, to_dev(kp), to_dev(vp), tables, lens, scale, int(lens.max()), keep)
+    assert torch.equal(_bits(kp1), _bits(kp2)) and torch.equal(_bits(vp1), _bits(vp2))
+    assert torch.equal(out1, out2)
+    keep_rows = slots >= 0
+    k_ref, v_ref = append_ref(k_new[keep_rows], v_new[keep_rows], slots[keep_rows], kp, vp)
+    assert np.array_equal(to_host(kp2).view(np.uint16), k_ref.view(np.uint16))
+    assert np.array_equal(to_host(vp2).view(np.uint16), v_ref.view(np.uint16))
+    ref = paged_decode_ref(q, k_ref, v_ref, tables, lens, scale)
+    assert_close(out2, ref, f"fused append + decode H={H} D={D} keep_cached={keep}")
+    assert not to_host(out2)[lens == 0].any()
+
+
+def test_batch200_fused_equals_separate():
+    """The headline batch (200 sequences, 32 heads x 128, contexts up to
+    2048, one new token each): fused and separate agree bit for bit, and
+    twelve sequences against the oracle."""
+    c = wl.gpt_batch(200, seed=2, append=True)
+    kp, vp = device_pools(c)
+    (kp1, vp1, out1), (kp2, vp2, out2), slots = _both_ways(
+        c.q, c.k_new, c.v_new, kp, vp, c.block_tables, c.context_lens, c.scale, c.max_context)
+    assert np.array_equal(slots, c.slot_mapping)
+    assert torch.equal(_bits(kp1), _bits(kp2)) and torch.equal(_bits(vp1), _bits(vp2))
+    assert torch.equal(out1, out2)
+    k_ref, v_ref = append_ref(c.k_new, c.v_new, c.slot_mapping, c.k_pool, c.v_pool)
+    seqs = list(range(0, 200, 17)) + [199]
+    ref = paged_decode_ref(c.q, k_ref, v_ref, c.block_tables, c.context_lens, c.scale, seqs=seqs)
+    assert_close(out2, ref, "fused append + decode, batch 200")
+
+
+def test_repeated_steps_grow_the_cache():
+    """Three fused steps in a row, each appending one more token per
+    sequence, equal three separate append + decode steps."""
+    H, D = 8, 128
+    rng = np.random.default_rng(95)
+    lens0 = np.array([14, 15, 16, 31, 200, 1], dtype=np.int32)
+    steps = 3
+    final = lens0 + steps
+    q, _, _, kp, vp, tables, _ = _ragged(96, H, D, list(final))
+    kp_a, vp_a = to_dev(kp), to_dev(vp)
+    kp_b, vp_b = kp_a.clone(), vp_a.clone()
+    scale = float(np.float32(D ** -0.5))
+    for s in range(1, steps + 1):
+        lens = lens0 + s
+        k_new = wl.normal_fp16(rng, (len(lens), H, D))
+        v_new = wl.normal_fp16(rng, (len(lens), H, D))
+        kv_append(to_dev(k_new), to_dev(v_new), to_dev(_last_slots(tables, lens)), kp_a, vp_a)
+        out_a = pa_decode(to_dev(q), kp_a, vp_a, to_dev(tables), to_dev(lens), scale,
+                          max_context_len=int(final.max()))
+        out_b = pa_decode_append(to_dev(q), to_dev(k_new), to_dev(v_new), kp_b, vp_b,
+                                 to_dev(tables), to_dev(lens), scale,
+                                 max_context_len=int(final.max()))
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), f"step {s}"
+    assert torch.equal(_bits(kp_a), _bits(kp_b)) and torch.equal(_bits(vp_a), _bits(vp_b))

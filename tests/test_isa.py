@@ -83,10 +83,14 @@ def tile_loops(body):
     return {k: v for k, v in loops.items() if "buffer_load_dwordx4" in v}
 
 
+@pytest.mark.parametrize("append", [0, 1])
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("policy", [2, 0])
-def test_flat_loop_never_drains_loads(flat_asm, D, policy):
-    body = kernel_body(flat_asm, f"pa_decode_flat_kernelILi{D}ELi{policy}ELb0E")
+def test_flat_loop_never_drains_loads(flat_asm, D, policy, append):
+    """The flat decode (and its instantiation with the fused append) keeps
+    its load ring going: no full drain of the load counter once blocks are
+    consumed."""
+    body = kernel_body(flat_asm, f"pa_decode_flat_kernelILi{D}ELi{policy}ELb0ELb{append}E")
     loops = tile_loops(body)
     assert loops, "no tile loop found"
     for label, text in loops.items():
@@ -109,13 +113,16 @@ def test_partition_loop_never_drains_loads(part_asm, D, policy):
 
 
 def test_no_spills_and_register_budget(flat_asm, part_asm):
-    for asm, name in ((flat_asm, "pa_decode_flat_kernelILi128ELi2ELb0E"),
+    for asm, name in ((flat_asm, "pa_decode_flat_kernelILi128ELi2ELb0ELb0E"),
+                      (flat_asm, "pa_decode_flat_kernelILi128ELi2ELb0ELb1E"),
                       (part_asm, "pa_decode_part_kernelILi128E")):
         assert meta(asm, name, "vgpr_spill_count") == 0
         assert meta(asm, name, "private_segment_fixed_size") == 0
-    # two waves per SIMD for the flat kernel (<= 256 VGPRs), three for the
-    # partitioned one (<= 168)
-    assert meta(flat_asm, "pa_decode_flat_kernelILi128ELi2ELb0E", "vgpr_count") <= 256
+    # two waves per SIMD for the flat kernel (<= 256 VGPRs), with or without
+    # the fused append, three for the partitioned one (<= 168)
+    for append in (0, 1):
+        name = f"pa_decode_flat_kernelILi128ELi2ELb0ELb{append}E"
+        assert meta(flat_asm, name, "vgpr_count") <= 256
     assert meta(part_asm, "pa_decode_part_kernelILi128E", "vgpr_count") <= 168
 
 
@@ -179,7 +186,7 @@ def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D):
 def test_contiguous_flat_loop_never_drains_loads(flat_asm, D):
     """The same flat kernel addressing contiguous rows: same load ring, no
     drain, no spill."""
-    name = f"pa_decode_flat_kernelILi{D}ELi2ELb1E"
+    name = f"pa_decode_flat_kernelILi{D}ELi2ELb1ELb0E"
     body = kernel_body(flat_asm, name)
     loops = tile_loops(body)
     assert loops
