@@ -348,24 +348,26 @@ __global__ __launch_bounds__(256) void pa_decode_flat_merge_kernel(FlatArgs a) {
   if (bh >= a.B * a.H) return;
   const int b = bh / a.H;
   const int h = bh % a.H;
+  _Float16* orow = a.out + (size_t)bh * D;
   const int T = a.ws_seq[a.B];
   const int S = a.ws_seq[b];
   const int E = a.ws_seq[b + 1];
-  _Float16* orow = a.out + (size_t)bh * D;
-  if (a.k_new != nullptr && E > S) {
+  if (a.k_new != nullptr) {
     // the fused append: the new token (already used by the decode kernel)
-    // goes to the sequence's last position, slot tail - 1 of its last block;
-    // lanes 0 .. D/8-1 write K, the next D/8 lanes V, 16 bytes each
+    // goes to the sequence's last position t, slot t % 16 of its last block;
+    // lanes 0 .. D/8-1 write K, the next D/8 lanes V, 16 bytes each.  The
+    // loads are issued unconditionally, ahead of the merge's own.
     const int ctx = clamp_ctx(a.context_lens[b], a.ctx_limit);
-    const int t = ctx - 1;
+    const int t = max(ctx - 1, 0);
     const int id = a.block_tables[(size_t)b * a.max_blocks + t / kBlockTokens];
-    const size_t blk = (size_t)min(max(id, 0), a.num_blocks - 1);
     const int g = lane % (D / 8);
-    if (lane < 2 * (D / 8)) {
-      const bool is_v = lane >= D / 8;
-      const u4v* src = reinterpret_cast<const u4v*>((is_v ? a.v_new : a.k_new) + (size_t)bh * D);
+    const bool is_v = lane >= D / 8;
+    const u4v row_new =
+        reinterpret_cast<const u4v*>((is_v ? a.v_new : a.k_new) + (size_t)bh * D)[g];
+    if (ctx > 0 && lane < 2 * (D / 8)) {
+      const size_t blk = (size_t)min(max(id, 0), a.num_blocks - 1);
       u4v* dst = reinterpret_cast<u4v*>(const_cast<void*>(is_v ? a.v_pool : a.k_pool));
-      dst[((blk * a.H + h) * (D / 8) + g) * kBlockTokens + t % kBlockTokens] = src[g];
+      dst[((blk * a.H + h) * (D / 8) + g) * kBlockTokens + t % kBlockTokens] = row_new;
     }
   }
   if (E == S) {
