@@ -144,12 +144,8 @@ struct GroupArgs {
 #ifndef PKV_PREFILL_WAVES
 #define PKV_PREFILL_WAVES 4
 #endif
-#ifndef PKV_PREFILL_TILES
-#define PKV_PREFILL_TILES 4
-#endif
 constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, 32 query rows each
 constexpr int kPrefillRows = 32 * kPrefillWaves;
-constexpr int kPrefillTiles = PKV_PREFILL_TILES;   // tiles in flight + 1 (a multiple of 4)
 constexpr int kPrefillMaxLdsBytes = 32 * 1024;
 
 struct PrefillArgs {

@@ -11,10 +11,11 @@
 // one head; each of its 4 waves serves 32 of them.  The workgroup streams
 // the blocks up to the one holding its last row's position once: every
 // (block, head) tile of K and V is fetched by the workgroup's threads
-// together (16 bytes each) through a register ring of kPrefillTiles tiles
-// and stored into one of four LDS stages (V slots past the context zeroed,
-// V token slots swizzled against bank conflicts); after every second tile a
-// barrier, then each wave consumes the pair (32 tokens) on the
+// together (16 bytes each) through a register ring of four tiles and stored
+// into one of three LDS pair slots (V slots past the context zeroed, V
+// token slots swizzled against bank conflicts); after every second tile a
+// barrier, then each wave consumes the pair (32 tokens), its score products
+// issued one pair ahead of its softmax, on the
 // v_mfma_f32_32x32x16_f16 matrix instruction, whose lane l holds row l%32
 // and k slots 8*(l/32) .. +7 of A, the same of B (column l%32), and C rows
 // 8*(r/4) + 4*(l/32) + r%4 of column l%32 in its register r:
@@ -125,13 +126,12 @@ void pa_prefill_kernel(PrefillArgs a) {
   constexpr int kThreads = 64 * kPrefillWaves;
   constexpr int kLoaders = 2 * kTileUnits < kThreads ? 2 * kTileUnits : kThreads;
   constexpr int kUnits = 2 * kTileUnits / kLoaders;     // 16-byte units per loading thread
-  constexpr int R = kPrefillTiles;
-  constexpr int kStages = 4;
-  static_assert(kUnits >= 1 && R % kStages == 0 && kLoaders % kWave == 0,
-                "tile split; four stages consumed in pairs; whole loading waves");
+  constexpr int R = 4;                                  // register ring: two pairs of tiles
+  constexpr int kSlots = 3;                             // LDS pair slots
+  static_assert(kUnits >= 1 && kLoaders % kWave == 0, "tile split; whole loading waves");
   extern __shared__ int smem[];
   __shared__ int s_wave[kPrefillWaves];
-  __shared__ u4v s_kv[kStages][2 * kTileUnits];         // stage: K tile, then V tile
+  __shared__ u4v s_kv[2 * kSlots][2 * kTileUnits];     // tile stage: K tile, then V tile
   int* s_group = smem;                                  // B + 1
   int* s_ids = smem + a.B + 1;                          // block ids of the sequence
 
@@ -180,7 +180,9 @@ void pa_prefill_kernel(PrefillArgs a) {
   // The scores are taken as (sign(scale) q) . k (an exact negation), so that
   // their maximum is the maximum of the scaled scores; weights are then
   // exp2(s * |scale log2 e| - m) with one fused multiply-add.
-  const float sabs = fabsf(a.scale_log2);
+  // (a zero scale is taken as the smallest normal float: the weights are
+  // then exactly 1, and a masked score's -inf times it stays -inf)
+  const float sabs = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
   if (a.scale_log2 < 0.0f) {
 #pragma unroll
     for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
@@ -241,40 +243,49 @@ void pa_prefill_kernel(PrefillArgs a) {
     const int tr_lo = v_slot(g0 * kBlockTokens + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
     const int tr_hi = v_slot(g0 * kBlockTokens + 8 + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
     // this lane's K row: token col of the pair (tile col / 16), dims 16i + 8hf ..
-    const int k_unit = (2 * 0 + hf) * kBlockTokens + col % 16;   // + 2i * 16 per MFMA
-    auto compute = [&](int sa, int j) {
-      if (!wave_rows) return;                           // uniform per wave
-      const int t0 = j * kBlockTokens;
-      const u4v* kt = s_kv[sa + col / 16];
-      u4v kr[kQK];                                      // A operands: token col of the pair
-#pragma unroll
-      for (int i = 0; i < kQK; ++i) kr[i] = kt[k_unit + 2 * i * kBlockTokens];
+    const int k_unit = hf * kBlockTokens + col % 16;    // + 2i * 16 per MFMA
+
+    // Score products of the pair in pair slot sl (tiles 2 sl, 2 sl + 1):
+    // S^T (32 tokens x 32 queries), register r = token 8*(r/4) + 4*hf + r%4.
+    auto scores = [&](int sl) {
       f16x16 sc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+      const u4v* kt = s_kv[2 * sl + col / 16];
+      u4v kr[kQK];                                      // A operands: token col of the pair
+#pragma unroll
+      for (int i = 0; i < kQK; ++i) kr[i] = kt[k_unit + 2 * i * kBlockTokens];
 #pragma unroll
       for (int i = 0; i < kQK; ++i)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(kr[i]), qb[i], sc, 0, 0, 0);
-      // register r: token tk = 8*(r/4) + 4*hf + r%4 of the pair (tile tk / 16).
+      return sc;
+    };
+
+    // Softmax of pair pp (blocks 2 pp, 2 pp + 1), first part: mask the
+    // scores (masked ones become -inf), raise the reference maximum if
+    // needed (rescaling the sums), return the reference for the weights.
+    // All the branches of the step are here, so that the rest of the step
+    // and the next pair's score products share one basic block.
+    auto prep = [&](f16x16& sc, int pp) {
+      const int j = 2 * pp;
+      const int t0 = j * kBlockTokens;
       // A pair wholly at or before the wave's first row (hence inside the
-      // context and visible to every row of the wave) needs no mask; the
-      // masked path gives the same result for the tokens it keeps.
+      // context and visible to every row of the wave) needs no mask.
       const bool full = t0 + 2 * kBlockTokens - 1 <= p_wave;   // uniform per wave
-      bool live[16];
-      float mx = kNegInf;
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      } else {
+      if (!full) {
         const int va = j < nblk ? min(kBlockTokens, ctx - t0) : 0;
         const int vb = j + 1 < nblk ? min(kBlockTokens, ctx - t0 - kBlockTokens) : 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int tk = 8 * (r / 4) + 4 * hf + r % 4;
-          live[r] = row_ok & (tk % kBlockTokens < (tk < kBlockTokens ? va : vb)) & (t0 + tk <= p_q);
-          mx = fmaxf(mx, live[r] ? sc[r] : kNegInf);
+          const bool live =
+              row_ok & (tk % kBlockTokens < (tk < kBlockTokens ? va : vb)) & (t0 + tk <= p_q);
+          sc[r] = live ? sc[r] : kNegInf;
         }
       }
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       auto sw = __builtin_amdgcn_permlane32_swap(as_u32(mx), as_u32(mx), false, false);
       mx = fmaxf(as_f32(sw[0]), as_f32(sw[1]));
       // The reference maximum m moves only when the pair's maximum exceeds it
@@ -289,18 +300,17 @@ void pa_prefill_kernel(PrefillArgs a) {
         l *= alpha;
         m = mxs;
       }
-      const float mref = m == kNegInf ? 0.0f : m;
+      return m == kNegInf ? 0.0f : m;
+    };
+
+    // Second part: the fp16 weights (exp2(s |scale log2 e| - mref); a
+    // masked score gives exp2(-inf) = 0), their running sum, and the value
+    // products of the pair in pair slot sl.
+    auto weights_pv = [&](const f16x16& sc, float mref, int sl) {
       h8v pb[2];
-      if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pb[r / 8][r % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], sabs, -mref));
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pb[r / 8][r % 8] =
-              (_Float16)__builtin_amdgcn_exp2f(live[r] ? fmaf(sc[r], sabs, -mref) : kNegInf);
-      }
+      for (int r = 0; r < 16; ++r)
+        pb[r / 8][r % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], sabs, -mref));
       // running sum of the rounded weights, two per instruction
       typedef _Float16 h2v __attribute__((ext_vector_type(2)));
       const h2v ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -315,7 +325,7 @@ void pa_prefill_kernel(PrefillArgs a) {
       for (int s = 0; s < kSl; ++s) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const _Float16* vt = reinterpret_cast<const _Float16*>(&s_kv[sa + kk][kTileUnits]);
+          const _Float16* vt = reinterpret_cast<const _Float16*>(&s_kv[2 * sl + kk][kTileUnits]);
           const int off = s * 4 * kBlockTokens * 8;       // 4 dim groups per slice
           const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s4v*)(vt + off + tr_lo));
@@ -327,24 +337,48 @@ void pa_prefill_kernel(PrefillArgs a) {
         }
       }
     };
-    // R tiles in flight in registers, four LDS stages: tile j + r of a
-    // round goes to stage r % 4, a barrier after each pair, then the pair is
-    // consumed.  A stage is rewritten only after the barrier that follows
-    // the last use of its previous tile.  Steps past the last block see
-    // valid = 0 (exact no-ops), so the loop runs whole rounds with no exit
-    // in its body.
+
+    // Software pipeline over pairs of blocks.  Pair p lives in LDS pair
+    // slot p % 3; its two tiles come through a register ring of four tiles
+    // (two pairs), fetched two pairs before they are staged.  Iteration p
+    // stages pair p + 1 and refetches its ring tiles for pair p + 3, meets
+    // the barrier, takes the branching part of pair p's softmax, then issues
+    // the score products of pair p + 1 in one basic block with the weights
+    // and value products of pair p, which do not depend on them.
+    // The slot staged in iteration p was last read in iteration p - 2, which
+    // every wave finished before the barrier of iteration p - 1.  Pairs past
+    // the last block see valid = 0 (exact no-ops), so the loop runs whole
+    // rounds of two pairs with no exit in its body.
     u4v ring[R][kUnits];
 #pragma unroll
-    for (int r = 0; r + 1 < R; ++r) fetch(ring[r], r);
-    for (int j = 0; j < nblk; j += R) {
+    for (int r = 0; r < R; ++r) fetch(ring[r], r);
+    stage(ring[0], 0, 0);
+    stage(ring[1], 1, 1);
+    fetch(ring[0], 4);
+    fetch(ring[1], 5);
+    __syncthreads();
+    f16x16 sc_cur = {};
+    if (wave_rows) sc_cur = scores(0);
+    const int npairs = (nblk + 1) / 2;
+    int sl = 0;                                         // pair slot of pair p
+    for (int p = 0; p < npairs; p += 2) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        fetch(ring[(r + R - 1) % R], j + r + R - 1);
-        stage(ring[r], r % kStages, j + r);
-        if (r % 2 == 1) {
-          __syncthreads();
-          compute((r - 1) % kStages, j + r - 1);
+      for (int u = 0; u < 2; ++u) {
+        const int pn = p + u + 1;                       // the pair staged now
+        const int sn = sl == kSlots - 1 ? 0 : sl + 1;
+        const int ra = (2 * (u + 1)) % R;               // its ring tiles
+        stage(ring[ra], 2 * sn, 2 * pn);
+        fetch(ring[ra], 2 * pn + R);
+        stage(ring[ra + 1], 2 * sn + 1, 2 * pn + 1);
+        fetch(ring[ra + 1], 2 * pn + 1 + R);
+        __syncthreads();
+        if (wave_rows) {                                // uniform per wave
+          const float mref = prep(sc_cur, p + u);
+          const f16x16 sc_next = scores(sn);
+          weights_pv(sc_cur, mref, sl);
+          sc_cur = sc_next;
         }
+        sl = sn;
       }
     }
   }
