@@ -408,6 +408,12 @@ int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
   a.num_blocks = num_blocks;
   a.group_size = group_size;
   a.part_blocks = pkv::kGroupPartBlocks;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return PKV_ERR_HIP;
+  a.slots = cus * pkv::kGroupSlotsPerCU;
   a.max_parts = plan.max_parts;
   a.head_groups = (H + pkv::kGroupWaves - 1) / pkv::kGroupWaves;
   a.keep_cached = (flags & PKV_DECODE_KEEP_KV_CACHED) != 0;

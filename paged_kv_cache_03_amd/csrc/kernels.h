@@ -115,6 +115,8 @@ constexpr int kMaxGroupPartBlocks = 64;    // longest partition, in positions (b
 constexpr int kGroupPartBlocks = PKV_GROUP_PART;   // partition length the launch plan asks for
 constexpr int kGroupGridTarget = PKV_GROUP_GRID;   // workgroups launched at most (grid-stride loop)
 constexpr int kGroupMaxLdsBytes = 48 * 1024;
+constexpr int kGroupItemCost = 8;          // an item's set-up, in positions (partition choice)
+constexpr int kGroupSlotsPerCU = 2;        // resident workgroups per CU (4 waves, <= 256 VGPRs)
 
 struct GroupArgs {
   const _Float16* q;
@@ -134,7 +136,8 @@ struct GroupArgs {
   int ctx_limit;
   int num_blocks;
   int group_size;      // members decoded per group (1..kGroupMaxMembers)
-  int part_blocks;     // partition length (positions) target
+  int part_blocks;     // shortest partition length (positions) the workspace allows
+  int slots;           // workgroups resident at once (the rounds the items fill)
   int max_parts;       // workspace capacity in partitions
   int head_groups;     // ceil(H / kGroupWaves)
   bool keep_cached;

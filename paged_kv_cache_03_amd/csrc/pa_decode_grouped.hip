@@ -12,9 +12,10 @@
 // logical blocks are the same physical blocks.  Its "positions" are the P
 // shared blocks (all n queries attend) followed by each member's private
 // blocks (only that member's query attends).  The positions of a group are
-// cut into near-equal partitions; a workgroup takes (partition, head group)
-// items in a grid-stride loop, one wave per head, and stages the item's
-// block ids and masks in LDS.
+// cut into near-equal partitions, whose length each call chooses from the
+// total so that the items fill whole rounds of the resident workgroups; a
+// workgroup takes (partition, head group) items in a grid-stride loop, one
+// wave per head, and stages the item's block ids and masks in LDS.
 //
 // Per 16-token tile the arithmetic is two small dense contractions on the
 // matrix cores, one MFMA column per member (pa_mfma.h).
@@ -64,22 +65,61 @@ __device__ __forceinline__ int group_parts(int npos, int part_blocks) {
   return (npos + part_blocks - 1) / part_blocks;
 }
 
-// s_part[g] = first partition of group g over all groups, s_part[G] = total.
-// All threads take part; ends with a barrier.
-__device__ void partition_prefix(const GroupArgs& a, int* s_part, int* s_wave) {
+// Partition length for this call, from the total number of positions:
+// items (partitions x head groups) are taken by the resident workgroups in
+// rounds, and a nearly empty last round costs as much as a full one.  For
+// R rounds the shortest length that keeps the items within R x slots is
+// ceil(hg * total / (R * slots - hg * G)) (a group's partitions are at most
+// npos / part + 1); take the R whose rounds are shortest overall, counting
+// an item's set-up as kGroupItemCost positions.  At least min_part (the
+// workspace is sized for it), at most kMaxGroupPartBlocks (LDS staging).
+__device__ int choose_part(long long total, int hg, int G, int slots, int min_part) {
+  int best = kMaxGroupPartBlocks;
+  long long best_cost = -1;
+  for (int R = 1; R <= 16; ++R) {
+    const long long room = (long long)R * slots - (long long)hg * G;
+    if (room <= 0) continue;
+    const long long part = max((long long)min_part, ((long long)hg * total + room - 1) / room);
+    if (part > kMaxGroupPartBlocks) continue;
+    const long long cost = R * (part + kGroupItemCost);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = (int)part;
+    }
+  }
+  return best;
+}
+
+// s_part[g] = first partition of group g over all groups, s_part[G] = total;
+// returns the partition length.  All threads take part; ends with a barrier.
+__device__ int partition_prefix(const GroupArgs& a, int* s_part, int* s_wave) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int per = (a.G + nt - 1) / nt;
   const int lo = min(a.G, tid * per);
   const int hi = min(a.G, lo + per);
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  // total positions over all groups, then the partition length
+  int pos = 0;
+  for (int g = lo; g < hi; ++g) {
+    s_part[g] = group_shape(a, g).npos;   // positions first, partitions below
+    pos += s_part[g];
+  }
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) pos += __shfl_xor(pos, d, kWave);
+  if (lane == 0) s_wave[wave] = pos;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < nt / kWave; ++w) total += s_wave[w];
+  const int part = choose_part(total, a.head_groups, a.G, a.slots, a.part_blocks);
+  __syncthreads();                     // s_wave is reused below
   int own = 0;
   for (int g = lo; g < hi; ++g) {
-    const int np = group_parts(group_shape(a, g).npos, a.part_blocks);
+    const int np = group_parts(s_part[g], part);
     s_part[g] = np;                    // counts first, offsets below
     own += np;
   }
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
   int incl = own;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -97,6 +137,7 @@ __device__ void partition_prefix(const GroupArgs& a, int* s_part, int* s_wave) {
   }
   if (tid == nt - 1) s_part[a.G] = run;
   __syncthreads();
+  return part;
 }
 
 // The group holding global partition gp: the largest g < G with
@@ -132,7 +173,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
   const int qc = lane % 16;            // query column (member) of this lane
   const int tg = lane / 16;            // token / dim quarter of this lane
 
-  partition_prefix(a, s_part, s_wave);
+  partition_prefix(a, s_part, s_wave);   // (the items' lengths follow from s_part)
   const int total_parts = min(s_part[a.G], a.max_parts);
   if (blockIdx.x == 0) {
     // per-sequence map for the merge: (first partition, partitions * 16 + member)
