@@ -653,6 +653,8 @@ def main():
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "seq_layers_per_s": round(run.seqs_per_step / (ms_per_step / 1e3), 1),
         "pa_decode_us": round(dec_avg_s * 1e6, 3),
+        "pa_decode_us_median": round(float(np.median(dec_ms)) * 1e3, 3),
+        "pa_decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
         "pa_decode_kv_gbs": round(dec_gbs, 2),
         "pa_decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
@@ -679,6 +681,8 @@ def main():
         result["value"] = round(pf["rows"] / (ms_per_step / 1e3), 1)
         result["unit"] = "tokens/s"
         result["pa_prefill_us"] = result.pop("pa_decode_us")
+        result["pa_prefill_us_median"] = result.pop("pa_decode_us_median")
+        result["pa_prefill_us_p90"] = result.pop("pa_decode_us_p90")
         result["pa_prefill_tflops"] = round(tflops, 2)
         result["pa_prefill_gbs"] = round(achieved, 2)
         for k in ("pa_decode_kv_gbs", "pa_decode_pct_hbm_peak", "pct_hbm_peak"):
