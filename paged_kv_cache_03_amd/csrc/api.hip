@@ -444,8 +444,8 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   if (pkv::prefill_lds_bytes(B, blocks_used) > (size_t)pkv::kPrefillMaxLdsBytes)
     return PKV_ERR_BAD_SHAPE;
   // query groups: sum over sequences of ceil(n_b / R) <= num_query_rows / R + B, R = kPrefillRows
-  const long long grid = ((long long)ceil_div(num_query_rows, pkv::kPrefillRows) + B) * H;
-  if (grid >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
+  const long long bound = ((long long)ceil_div(num_query_rows, pkv::kPrefillRows) + B) * H;
+  if (bound >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out)
     return PKV_ERR_NULL_PTR;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
@@ -466,7 +466,18 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = max_context_len;
   a.num_blocks = num_blocks;
-  const hipError_t e = pkv::launch_pa_prefill(a, D, (int)grid, blocks_used,
+  // the items run in a grid-stride loop over at most eight workgroups per
+  // resident slot: few enough that no workgroup is launched only to find no
+  // item, enough that the hardware's dispatch still balances items of
+  // unequal length; a multiple of 8, so item i stays on XCD i % 8
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return PKV_ERR_HIP;
+  const long long resident = (long long)cus * pkv::kPrefillSlotsPerCU * 8 / 8 * 8;
+  const int grid = (int)(bound < resident ? bound : (resident > 0 ? resident : bound));
+  const hipError_t e = pkv::launch_pa_prefill(a, D, grid, blocks_used,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -150,6 +150,7 @@ struct GroupArgs {
 constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, 32 query rows each
 constexpr int kPrefillRows = 32 * kPrefillWaves;
 constexpr int kPrefillMaxLdsBytes = 32 * 1024;
+constexpr int kPrefillSlotsPerCU = 2;      // resident workgroups per CU (two waves per SIMD)
 
 struct PrefillArgs {
   const _Float16* q;            // [num_rows][H][D]

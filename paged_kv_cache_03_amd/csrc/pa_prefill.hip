@@ -33,9 +33,10 @@
 //    4h .. 4h+3 and 8+4h .. 8+4h+3).
 // Blocks past a row's position are exact no-ops for it (causal mask per
 // element), so a row's result does not depend on the rows it shares a
-// workgroup with.  Workgroup i serves head i % H (one XCD per head when H is
-// a multiple of 8), and within a sequence the groups that reach furthest
-// are dispatched first.
+// workgroup with.  Workgroups take (query group, head) items in a
+// grid-stride loop; item i serves head i % H, and with a grid that is a
+// multiple of 8 it runs on XCD i % 8 (one XCD per head when H is a multiple
+// of 8).  Within a sequence the groups that reach furthest come first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -142,263 +143,269 @@ void pa_prefill_kernel(PrefillArgs a) {
   const int hf = lane / 32;                             // k-slot half of this lane
 
   group_prefix(a, s_group, s_wave);
-  const int gt = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
-  if (gt >= s_group[a.B]) return;                       // uniform for the workgroup
-  const int b = seq_of_group(s_group, a.B, gt);
-  const int n = rows_of(a, b);
-  const int kq = groups_of(a, b) - 1 - (gt - s_group[b]);   // furthest-reaching group first
-  const int ctx = clampi(a.context_lens[b], 0, a.ctx_limit);
-  const int row0 = kPrefillRows * kq;
-  const int grows = min(kPrefillRows, n - row0);
-  const int p_group = ctx - n + row0;                   // position of the group's first row
-  const int p_last = min(p_group + grows - 1, ctx - 1);
-  const int nblk = p_last >= 0 ? p_last / kBlockTokens + 1 : 0;
+  // Items (query group, head), longest-reaching groups first, in a
+  // grid-stride loop: the prefix above is computed once per workgroup for
+  // its few items, and no workgroup is launched only to find none.
+  const int items = s_group[a.B] * a.H;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int gt = item / a.H;
+    const int h = item % a.H;
+    const int b = seq_of_group(s_group, a.B, gt);
+    const int n = rows_of(a, b);
+    const int kq = groups_of(a, b) - 1 - (gt - s_group[b]);   // furthest-reaching group first
+    const int ctx = clampi(a.context_lens[b], 0, a.ctx_limit);
+    const int row0 = kPrefillRows * kq;
+    const int grows = min(kPrefillRows, n - row0);
+    const int p_group = ctx - n + row0;                   // position of the group's first row
+    const int p_last = min(p_group + grows - 1, ctx - 1);
+    const int nblk = p_last >= 0 ? p_last / kBlockTokens + 1 : 0;
 
-  for (int j = tid; j < nblk; j += blockDim.x) {
-    const int id = a.block_tables[(size_t)b * a.max_blocks + j];
-    s_ids[j] = clampi(id, 0, a.num_blocks - 1);
-  }
-  __syncthreads();
-
-  // this lane's query row: wave w serves rows row0 + 32w ..; a wave with no
-  // row skips the arithmetic (it still loads, stages and meets the barriers)
-  const bool wave_rows = 32 * wave < grows;
-  const int wrow = 32 * wave + col;
-  const int qrow = a.query_start[b] + row0 + wrow;
-  const bool row_ok = wrow < grows && qrow >= 0 && qrow < a.num_rows;
-  const int p_q = p_group + wrow;
-  const rsrc_t qr = make_rsrc(a.q, (uint32_t)((size_t)a.num_rows * a.H * D * 2));
-  const uint32_t qoff = row_ok ? (uint32_t)((((size_t)qrow * a.H + h) * D + 8 * hf) * 2)
-                               : 0xFFFFFFF0u;           // past the resource: reads 0
-  h8v qb[kQK];                                          // B operands: dims 16i + 8hf ..
-#pragma unroll
-  for (int i = 0; i < kQK; ++i)
-    qb[i] = as_h8(__builtin_amdgcn_raw_buffer_load_b128(qr, qoff + (row_ok ? i * 32 : 0), 0, 0));
-  // keep the query loads ahead of the ring's first tiles (every step reads them)
-  __builtin_amdgcn_sched_barrier(0);
-  // The scores are taken as (sign(scale) q) . k (an exact negation), so that
-  // their maximum is the maximum of the scaled scores; weights are then
-  // exp2(s * |scale log2 e| - m) with one fused multiply-add.
-  // (a zero scale is taken as the smallest normal float: the weights are
-  // then exactly 1, and a masked score's -inf times it stays -inf)
-  const float sabs = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
-  if (a.scale_log2 < 0.0f) {
-#pragma unroll
-    for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
-  }
-  const int p_wave = p_group + 32 * wave;               // position of the wave's first row
-
-  float m = kNegInf, l = 0.0f;        // reference maximum (scaled, log2); sum over this lane's tokens
-  f16x16 acc[kSl];
-#pragma unroll
-  for (int s = 0; s < kSl; ++s)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
-
-  if (nblk > 0) {
-    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
-    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
-    const size_t block_stride = (size_t)a.H * kTile;
-    // The tile pair is 2 * kTileUnits 16-byte units; the first kLoaders
-    // threads load them, unit u = tid + kLoaders * k (K for u < kTileUnits,
-    // V after).  kTileUnits and kLoaders are multiples of 64, so the choice
-    // of K or V is uniform per wave and the buffer resource stays in scalar
-    // registers.
-    const bool loader = wave * kWave < kLoaders;        // uniform per wave
-    auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
-    const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
-    auto fetch = [&](u4v (&r)[kUnits], int j) {
-      const int jj = min(j, nblk - 1);
-      const uint32_t bytes = j < nblk && loader ? kTile : 0u;
-      const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
-#pragma unroll
-      for (int k = 0; k < kUnits; ++k)
-        r[k] = __builtin_amdgcn_raw_buffer_load_b128(
-            make_rsrc((unit_is_v(k) ? vbase : kbase) + o, bytes), unit_off, 0, 0);
-    };
-    auto stage = [&](const u4v (&r)[kUnits], int st, int j) {
-      const int valid = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
-      if (!loader) return;                              // uniform per wave
-#pragma unroll
-      for (int k = 0; k < kUnits; ++k) {
-        u4v w = r[k];
-        // a V unit holds 8 dims of token (tid % kTileUnits) % 16
-        const int u = tid % kTileUnits;
-        const bool is_v = unit_is_v(k);
-        const bool zero = is_v && u % kBlockTokens >= valid;
-        w.x = zero ? 0u : w.x;
-        w.y = zero ? 0u : w.y;
-        w.z = zero ? 0u : w.z;
-        w.w = zero ? 0u : w.w;
-        s_kv[st][is_v ? kTileUnits + v_slot(u) : u] = w;
-      }
-    };
-    // transpose reads (offsets in halves inside a V tile): lane i = l%16 of
-    // its 16-lane group addresses dims 8*g + 4*(i%2) .. +3 of token
-    // 4hf + i/4 (lo) and of token 8 + 4hf + i/4 (hi), g = 2*(col/16) +
-    // (i%4)/2 (+ 4 per slice of 32 dims), at the swizzled slots
-    const int qi = lane % 16;
-    const int g0 = 2 * (col / 16) + (qi & 3) / 2;
-    const int tr_lo = v_slot(g0 * kBlockTokens + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
-    const int tr_hi = v_slot(g0 * kBlockTokens + 8 + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
-    // this lane's K row: token col of the pair (tile col / 16), dims 16i + 8hf ..
-    const int k_unit = hf * kBlockTokens + col % 16;    // + 2i * 16 per MFMA
-
-    // Score products of the pair in pair slot sl (tiles 2 sl, 2 sl + 1):
-    // S^T (32 tokens x 32 queries), register r = token 8*(r/4) + 4*hf + r%4.
-    auto scores = [&](int sl) {
-      f16x16 sc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
-      const u4v* kt = s_kv[2 * sl + col / 16];
-      u4v kr[kQK];                                      // A operands: token col of the pair
-#pragma unroll
-      for (int i = 0; i < kQK; ++i) kr[i] = kt[k_unit + 2 * i * kBlockTokens];
-#pragma unroll
-      for (int i = 0; i < kQK; ++i)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(kr[i]), qb[i], sc, 0, 0, 0);
-      return sc;
-    };
-
-    // Softmax of pair pp (blocks 2 pp, 2 pp + 1), first part: mask the
-    // scores (masked ones become -inf), raise the reference maximum if
-    // needed (rescaling the sums), return the reference for the weights.
-    // All the branches of the step are here, so that the rest of the step
-    // and the next pair's score products share one basic block.
-    auto prep = [&](f16x16& sc, int pp) {
-      const int j = 2 * pp;
-      const int t0 = j * kBlockTokens;
-      // A pair wholly at or before the wave's first row (hence inside the
-      // context and visible to every row of the wave) needs no mask.
-      const bool full = t0 + 2 * kBlockTokens - 1 <= p_wave;   // uniform per wave
-      if (!full) {
-        const int va = j < nblk ? min(kBlockTokens, ctx - t0) : 0;
-        const int vb = j + 1 < nblk ? min(kBlockTokens, ctx - t0 - kBlockTokens) : 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tk = 8 * (r / 4) + 4 * hf + r % 4;
-          const bool live =
-              row_ok & (tk % kBlockTokens < (tk < kBlockTokens ? va : vb)) & (t0 + tk <= p_q);
-          sc[r] = live ? sc[r] : kNegInf;
-        }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      auto sw = __builtin_amdgcn_permlane32_swap(as_u32(mx), as_u32(mx), false, false);
-      mx = fmaxf(as_f32(sw[0]), as_f32(sw[1]));
-      // The reference maximum m moves only when the pair's maximum exceeds it
-      // by more than kRescaleSlack, so the weights stay below 2^kRescaleSlack
-      // and the accumulators are rescaled rarely.  Both lanes of a row take
-      // the same decision.
-      const float mxs = mx == kNegInf ? kNegInf : mx * sabs;
-      if (mxs > m + kRescaleSlack) {
-        const float alpha = __builtin_amdgcn_exp2f(m - mxs);   // m = -inf: 0
-#pragma unroll
-        for (int s = 0; s < kSl; ++s) acc[s] = acc[s] * alpha;
-        l *= alpha;
-        m = mxs;
-      }
-      return m == kNegInf ? 0.0f : m;
-    };
-
-    // Second part: the fp16 weights (exp2(s |scale log2 e| - mref); a
-    // masked score gives exp2(-inf) = 0), their running sum, and the value
-    // products of the pair in pair slot sl.
-    auto weights_pv = [&](const f16x16& sc, float mref, int sl) {
-      h8v pb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pb[r / 8][r % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], sabs, -mref));
-      // running sum of the rounded weights, two per instruction
-      typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-      const h2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const h2v two = {pb[kk][e], pb[kk][e + 1]};
-          l = __builtin_amdgcn_fdot2(two, ones, l, false);
-        }
-#pragma unroll
-      for (int s = 0; s < kSl; ++s) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const _Float16* vt = reinterpret_cast<const _Float16*>(&s_kv[2 * sl + kk][kTileUnits]);
-          const int off = s * 4 * kBlockTokens * 8;       // 4 dim groups per slice
-          const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s4v*)(vt + off + tr_lo));
-          const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s4v*)(vt + off + tr_hi));
-          const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, both), pb[kk],
-                                                          acc[s], 0, 0, 0);
-        }
-      }
-    };
-
-    // Software pipeline over pairs of blocks.  Pair p lives in LDS pair
-    // slot p % 3; its two tiles come through a register ring of four tiles
-    // (two pairs), fetched two pairs before they are staged.  Iteration p
-    // stages pair p + 1 and refetches its ring tiles for pair p + 3, meets
-    // the barrier, takes the branching part of pair p's softmax, then issues
-    // the score products of pair p + 1 in one basic block with the weights
-    // and value products of pair p, which do not depend on them.
-    // The slot staged in iteration p was last read in iteration p - 2, which
-    // every wave finished before the barrier of iteration p - 1.  Pairs past
-    // the last block see valid = 0 (exact no-ops), so the loop runs whole
-    // rounds of two pairs with no exit in its body.
-    u4v ring[R][kUnits];
-#pragma unroll
-    for (int r = 0; r < R; ++r) fetch(ring[r], r);
-    stage(ring[0], 0, 0);
-    stage(ring[1], 1, 1);
-    fetch(ring[0], 4);
-    fetch(ring[1], 5);
+    for (int j = tid; j < nblk; j += blockDim.x) {
+      const int id = a.block_tables[(size_t)b * a.max_blocks + j];
+      s_ids[j] = clampi(id, 0, a.num_blocks - 1);
+    }
     __syncthreads();
-    f16x16 sc_cur = {};
-    if (wave_rows) sc_cur = scores(0);
-    const int npairs = (nblk + 1) / 2;
-    int sl = 0;                                         // pair slot of pair p
-    for (int p = 0; p < npairs; p += 2) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pn = p + u + 1;                       // the pair staged now
-        const int sn = sl == kSlots - 1 ? 0 : sl + 1;
-        const int ra = (2 * (u + 1)) % R;               // its ring tiles
-        stage(ring[ra], 2 * sn, 2 * pn);
-        fetch(ring[ra], 2 * pn + R);
-        stage(ring[ra + 1], 2 * sn + 1, 2 * pn + 1);
-        fetch(ring[ra + 1], 2 * pn + 1 + R);
-        __syncthreads();
-        if (wave_rows) {                                // uniform per wave
-          const float mref = prep(sc_cur, p + u);
-          const f16x16 sc_next = scores(sn);
-          weights_pv(sc_cur, mref, sl);
-          sc_cur = sc_next;
+
+    // this lane's query row: wave w serves rows row0 + 32w ..; a wave with no
+    // row skips the arithmetic (it still loads, stages and meets the barriers)
+    const bool wave_rows = 32 * wave < grows;
+    const int wrow = 32 * wave + col;
+    const int qrow = a.query_start[b] + row0 + wrow;
+    const bool row_ok = wrow < grows && qrow >= 0 && qrow < a.num_rows;
+    const int p_q = p_group + wrow;
+    const rsrc_t qr = make_rsrc(a.q, (uint32_t)((size_t)a.num_rows * a.H * D * 2));
+    const uint32_t qoff = row_ok ? (uint32_t)((((size_t)qrow * a.H + h) * D + 8 * hf) * 2)
+                                 : 0xFFFFFFF0u;           // past the resource: reads 0
+    h8v qb[kQK];                                          // B operands: dims 16i + 8hf ..
+  #pragma unroll
+    for (int i = 0; i < kQK; ++i)
+      qb[i] = as_h8(__builtin_amdgcn_raw_buffer_load_b128(qr, qoff + (row_ok ? i * 32 : 0), 0, 0));
+    // keep the query loads ahead of the ring's first tiles (every step reads them)
+    __builtin_amdgcn_sched_barrier(0);
+    // The scores are taken as (sign(scale) q) . k (an exact negation), so that
+    // their maximum is the maximum of the scaled scores; weights are then
+    // exp2(s * |scale log2 e| - m) with one fused multiply-add.
+    // (a zero scale is taken as the smallest normal float: the weights are
+    // then exactly 1, and a masked score's -inf times it stays -inf)
+    const float sabs = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+    if (a.scale_log2 < 0.0f) {
+  #pragma unroll
+      for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
+    }
+    const int p_wave = p_group + 32 * wave;               // position of the wave's first row
+
+    float m = kNegInf, l = 0.0f;        // reference maximum (scaled, log2); sum over this lane's tokens
+    f16x16 acc[kSl];
+  #pragma unroll
+    for (int s = 0; s < kSl; ++s)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+
+    if (nblk > 0) {
+      const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
+      const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
+      const size_t block_stride = (size_t)a.H * kTile;
+      // The tile pair is 2 * kTileUnits 16-byte units; the first kLoaders
+      // threads load them, unit u = tid + kLoaders * k (K for u < kTileUnits,
+      // V after).  kTileUnits and kLoaders are multiples of 64, so the choice
+      // of K or V is uniform per wave and the buffer resource stays in scalar
+      // registers.
+      const bool loader = wave * kWave < kLoaders;        // uniform per wave
+      auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
+      const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
+      auto fetch = [&](u4v (&r)[kUnits], int j) {
+        const int jj = min(j, nblk - 1);
+        const uint32_t bytes = j < nblk && loader ? kTile : 0u;
+        const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
+  #pragma unroll
+        for (int k = 0; k < kUnits; ++k)
+          r[k] = __builtin_amdgcn_raw_buffer_load_b128(
+              make_rsrc((unit_is_v(k) ? vbase : kbase) + o, bytes), unit_off, 0, 0);
+      };
+      auto stage = [&](const u4v (&r)[kUnits], int st, int j) {
+        const int valid = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
+        if (!loader) return;                              // uniform per wave
+  #pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+          u4v w = r[k];
+          // a V unit holds 8 dims of token (tid % kTileUnits) % 16
+          const int u = tid % kTileUnits;
+          const bool is_v = unit_is_v(k);
+          const bool zero = is_v && u % kBlockTokens >= valid;
+          w.x = zero ? 0u : w.x;
+          w.y = zero ? 0u : w.y;
+          w.z = zero ? 0u : w.z;
+          w.w = zero ? 0u : w.w;
+          s_kv[st][is_v ? kTileUnits + v_slot(u) : u] = w;
         }
-        sl = sn;
+      };
+      // transpose reads (offsets in halves inside a V tile): lane i = l%16 of
+      // its 16-lane group addresses dims 8*g + 4*(i%2) .. +3 of token
+      // 4hf + i/4 (lo) and of token 8 + 4hf + i/4 (hi), g = 2*(col/16) +
+      // (i%4)/2 (+ 4 per slice of 32 dims), at the swizzled slots
+      const int qi = lane % 16;
+      const int g0 = 2 * (col / 16) + (qi & 3) / 2;
+      const int tr_lo = v_slot(g0 * kBlockTokens + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
+      const int tr_hi = v_slot(g0 * kBlockTokens + 8 + 4 * hf + (qi >> 2)) * 8 + 4 * (qi & 1);
+      // this lane's K row: token col of the pair (tile col / 16), dims 16i + 8hf ..
+      const int k_unit = hf * kBlockTokens + col % 16;    // + 2i * 16 per MFMA
+
+      // Score products of the pair in pair slot sl (tiles 2 sl, 2 sl + 1):
+      // S^T (32 tokens x 32 queries), register r = token 8*(r/4) + 4*hf + r%4.
+      auto scores = [&](int sl) {
+        f16x16 sc;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+        const u4v* kt = s_kv[2 * sl + col / 16];
+        u4v kr[kQK];                                      // A operands: token col of the pair
+  #pragma unroll
+        for (int i = 0; i < kQK; ++i) kr[i] = kt[k_unit + 2 * i * kBlockTokens];
+  #pragma unroll
+        for (int i = 0; i < kQK; ++i)
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(kr[i]), qb[i], sc, 0, 0, 0);
+        return sc;
+      };
+
+      // Softmax of pair pp (blocks 2 pp, 2 pp + 1), first part: mask the
+      // scores (masked ones become -inf), raise the reference maximum if
+      // needed (rescaling the sums), return the reference for the weights.
+      // All the branches of the step are here, so that the rest of the step
+      // and the next pair's score products share one basic block.
+      auto prep = [&](f16x16& sc, int pp) {
+        const int j = 2 * pp;
+        const int t0 = j * kBlockTokens;
+        // A pair wholly at or before the wave's first row (hence inside the
+        // context and visible to every row of the wave) needs no mask.
+        const bool full = t0 + 2 * kBlockTokens - 1 <= p_wave;   // uniform per wave
+        if (!full) {
+          const int va = j < nblk ? min(kBlockTokens, ctx - t0) : 0;
+          const int vb = j + 1 < nblk ? min(kBlockTokens, ctx - t0 - kBlockTokens) : 0;
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tk = 8 * (r / 4) + 4 * hf + r % 4;
+            const bool live =
+                row_ok & (tk % kBlockTokens < (tk < kBlockTokens ? va : vb)) & (t0 + tk <= p_q);
+            sc[r] = live ? sc[r] : kNegInf;
+          }
+        }
+        float mx = kNegInf;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        auto sw = __builtin_amdgcn_permlane32_swap(as_u32(mx), as_u32(mx), false, false);
+        mx = fmaxf(as_f32(sw[0]), as_f32(sw[1]));
+        // The reference maximum m moves only when the pair's maximum exceeds it
+        // by more than kRescaleSlack, so the weights stay below 2^kRescaleSlack
+        // and the accumulators are rescaled rarely.  Both lanes of a row take
+        // the same decision.
+        const float mxs = mx == kNegInf ? kNegInf : mx * sabs;
+        if (mxs > m + kRescaleSlack) {
+          const float alpha = __builtin_amdgcn_exp2f(m - mxs);   // m = -inf: 0
+  #pragma unroll
+          for (int s = 0; s < kSl; ++s) acc[s] = acc[s] * alpha;
+          l *= alpha;
+          m = mxs;
+        }
+        return m == kNegInf ? 0.0f : m;
+      };
+
+      // Second part: the fp16 weights (exp2(s |scale log2 e| - mref); a
+      // masked score gives exp2(-inf) = 0), their running sum, and the value
+      // products of the pair in pair slot sl.
+      auto weights_pv = [&](const f16x16& sc, float mref, int sl) {
+        h8v pb[2];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pb[r / 8][r % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], sabs, -mref));
+        // running sum of the rounded weights, two per instruction
+        typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+        const h2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  #pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const h2v two = {pb[kk][e], pb[kk][e + 1]};
+            l = __builtin_amdgcn_fdot2(two, ones, l, false);
+          }
+  #pragma unroll
+        for (int s = 0; s < kSl; ++s) {
+  #pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const _Float16* vt = reinterpret_cast<const _Float16*>(&s_kv[2 * sl + kk][kTileUnits]);
+            const int off = s * 4 * kBlockTokens * 8;       // 4 dim groups per slice
+            const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s4v*)(vt + off + tr_lo));
+            const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s4v*)(vt + off + tr_hi));
+            const s8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, both), pb[kk],
+                                                            acc[s], 0, 0, 0);
+          }
+        }
+      };
+
+      // Software pipeline over pairs of blocks.  Pair p lives in LDS pair
+      // slot p % 3; its two tiles come through a register ring of four tiles
+      // (two pairs), fetched two pairs before they are staged.  Iteration p
+      // stages pair p + 1 and refetches its ring tiles for pair p + 3, meets
+      // the barrier, takes the branching part of pair p's softmax, then issues
+      // the score products of pair p + 1 in one basic block with the weights
+      // and value products of pair p, which do not depend on them.
+      // The slot staged in iteration p was last read in iteration p - 2, which
+      // every wave finished before the barrier of iteration p - 1.  Pairs past
+      // the last block see valid = 0 (exact no-ops), so the loop runs whole
+      // rounds of two pairs with no exit in its body.
+      u4v ring[R][kUnits];
+  #pragma unroll
+      for (int r = 0; r < R; ++r) fetch(ring[r], r);
+      stage(ring[0], 0, 0);
+      stage(ring[1], 1, 1);
+      fetch(ring[0], 4);
+      fetch(ring[1], 5);
+      __syncthreads();
+      f16x16 sc_cur = {};
+      if (wave_rows) sc_cur = scores(0);
+      const int npairs = (nblk + 1) / 2;
+      int sl = 0;                                         // pair slot of pair p
+      for (int p = 0; p < npairs; p += 2) {
+  #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int pn = p + u + 1;                       // the pair staged now
+          const int sn = sl == kSlots - 1 ? 0 : sl + 1;
+          const int ra = (2 * (u + 1)) % R;               // its ring tiles
+          stage(ring[ra], 2 * sn, 2 * pn);
+          fetch(ring[ra], 2 * pn + R);
+          stage(ring[ra + 1], 2 * sn + 1, 2 * pn + 1);
+          fetch(ring[ra + 1], 2 * pn + 1 + R);
+          __syncthreads();
+          if (wave_rows) {                                // uniform per wave
+            const float mref = prep(sc_cur, p + u);
+            const f16x16 sc_next = scores(sn);
+            weights_pv(sc_cur, mref, sl);
+            sc_cur = sc_next;
+          }
+          sl = sn;
+        }
       }
     }
-  }
 
-  // rows at a negative position (more queries than cached tokens) are zero;
-  // lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row
-  auto sw = __builtin_amdgcn_permlane32_swap(as_u32(l), as_u32(l), false, false);
-  l = as_f32(sw[0]) + as_f32(sw[1]);
-  if (row_ok) {
-    const float inv = p_q >= 0 && l > 0.0f ? 1.0f / l : 0.0f;
-    _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * hf;
-#pragma unroll
-    for (int s = 0; s < kSl; ++s)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        h4v o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][4 * q + r] * inv);
-        *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
-      }
+    // rows at a negative position (more queries than cached tokens) are zero;
+    // lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row
+    auto sw = __builtin_amdgcn_permlane32_swap(as_u32(l), as_u32(l), false, false);
+    l = as_f32(sw[0]) + as_f32(sw[1]);
+    if (row_ok) {
+      const float inv = p_q >= 0 && l > 0.0f ? 1.0f / l : 0.0f;
+      _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * hf;
+  #pragma unroll
+      for (int s = 0; s < kSl; ++s)
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h4v o;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][4 * q + r] * inv);
+          *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
+        }
+    }
+    __syncthreads();                                    // LDS staging is reused by the next item
   }
 }
 
