@@ -249,7 +249,8 @@ int pkv_cow_copy_blocks(void* const* k_pools, void* const* v_pools,
  *         context_lens, group_offsets (num_groups + 1 entries),
  *         group_shared_blocks (num_groups entries), workspace (256-byte
  *         aligned, at least pkv_pa_decode_grouped_workspace_size bytes).
- * host:   num_groups >= 0 (at most 12287); 1 <= group_size <= 16; the
+ * host:   num_groups >= 0 (at most 11259: the group offsets are staged in
+ *         on-chip memory); 1 <= group_size <= 16; the
  *         other sizes, block_size, max_context_len and flags as for
  *         pkv_pa_decode_ex (PKV_DECODE_KEEP_KV_CACHED is accepted; shared
  *         blocks are read once either way).

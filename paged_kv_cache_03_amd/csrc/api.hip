@@ -102,32 +102,43 @@ bool decode_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx) {
 // and its positions at most the blocks of its members, so all groups together
 // have at most ceil(B * max_blocks / part) + G partitions.
 struct GroupPlan {
-  int32_t max_parts = 0;
-  size_t map_bytes = 0;
+  int32_t nr = 0;          // ranges per head group
+  int32_t max_chunk = 0;   // longest range, in positions
+  size_t map_bytes = 0;    // workspace: per-sequence map, then group offsets, (m, l), acc
+  size_t gpos_bytes = 0;
   size_t ml_bytes = 0;
   size_t total = 0;
 };
 
-bool group_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t G,
-                    int32_t group_size) {
-  return decode_shape_ok(B, H, D, max_ctx) && G >= 0 &&
-         pkv::grouped_lds_bytes(G) <= (size_t)pkv::kGroupMaxLdsBytes && group_size >= 1 &&
-         group_size <= pkv::kGroupMaxMembers &&
-         (long long)B * H * D * 2 < (1LL << 32);
-}
-
+// Positions of all groups at most B * ceil(max_ctx / 16); the grid asks for
+// kGroupGridTarget workgroups, more ranges if a range's staging would not
+// fit LDS.  Returns nr = 0 when even single-position ranges would not.
 GroupPlan make_group_plan(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t G,
                           int32_t group_size) {
   GroupPlan p;
-  const long long parts =
-      ((long long)B * ceil_div(max_ctx, kBlockTokens) + pkv::kGroupPartBlocks - 1) /
-          pkv::kGroupPartBlocks + G;
-  p.max_parts = (int32_t)(parts < (1LL << 30) ? parts : (1LL << 30));
-  const size_t pieces = (size_t)p.max_parts * group_size * H;
-  p.map_bytes = round_up((size_t)B * 2 * sizeof(int32_t), kWsAlign);
+  const long long hg = (H + pkv::kGroupWaves - 1) / pkv::kGroupWaves;
+  const long long t_max = (long long)B * ceil_div(max_ctx, kBlockTokens);
+  const long long cap = ((long long)pkv::kGroupMaxLdsBytes / 4 - G - 1) / 4;   // positions
+  if (cap <= 0) return p;
+  long long nr = pkv::kGroupGridTarget / hg > 0 ? pkv::kGroupGridTarget / hg : 1;
+  if ((t_max + nr - 1) / nr > cap) nr = (t_max + cap - 1) / cap;
+  if (nr * hg >= (1LL << 31)) return p;
+  p.nr = (int32_t)nr;
+  p.max_chunk = (int32_t)((t_max + nr - 1) / nr);
+  const size_t pieces = (size_t)H * nr * 2 * group_size;
+  p.map_bytes = round_up((size_t)B * sizeof(int32_t), kWsAlign);
+  p.gpos_bytes = round_up(((size_t)G + 1) * sizeof(int32_t), kWsAlign);
   p.ml_bytes = round_up(pieces * 2 * sizeof(float), kWsAlign);
-  p.total = p.map_bytes + p.ml_bytes + pieces * D * sizeof(float);
+  p.total = p.map_bytes + p.gpos_bytes + p.ml_bytes + pieces * D * sizeof(float);
   return p;
+}
+
+bool group_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t G,
+                    int32_t group_size) {
+  return decode_shape_ok(B, H, D, max_ctx) && G >= 0 && group_size >= 1 &&
+         group_size <= pkv::kGroupMaxMembers && (long long)B * H * D * 2 < (1LL << 32) &&
+         (long long)B * ceil_div(max_ctx, kBlockTokens) < (1LL << 31) &&
+         make_group_plan(B, H, D, max_ctx, G, group_size).nr > 0;
 }
 
 }  // namespace
@@ -397,8 +408,9 @@ int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
   a.out = static_cast<_Float16*>(out);
   char* ws = static_cast<char*>(workspace);
   a.ws_map = reinterpret_cast<int*>(ws);
-  a.ws_ml = reinterpret_cast<float*>(ws + plan.map_bytes);
-  a.ws_acc = reinterpret_cast<float*>(ws + plan.map_bytes + plan.ml_bytes);
+  a.ws_gpos = reinterpret_cast<int*>(ws + plan.map_bytes);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.map_bytes + plan.gpos_bytes);
+  a.ws_acc = reinterpret_cast<float*>(ws + plan.map_bytes + plan.gpos_bytes + plan.ml_bytes);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.B = B;
   a.H = H;
@@ -407,21 +419,13 @@ int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
   a.ctx_limit = max_context_len;
   a.num_blocks = num_blocks;
   a.group_size = group_size;
-  a.part_blocks = pkv::kGroupPartBlocks;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return PKV_ERR_HIP;
-  a.slots = cus * pkv::kGroupSlotsPerCU;
-  a.max_parts = plan.max_parts;
   a.head_groups = (H + pkv::kGroupWaves - 1) / pkv::kGroupWaves;
+  a.nr = plan.nr;
+  a.max_chunk = plan.max_chunk;
+  const long long t_cap = (long long)plan.nr * plan.max_chunk;
+  a.t_cap = (int)(t_cap < 0x7fffffffLL ? t_cap : 0x7fffffffLL);
   a.keep_cached = (flags & PKV_DECODE_KEEP_KV_CACHED) != 0;
-  // workgroup 0 always runs: it writes the per-sequence map the merge reads
-  const long long items = (long long)plan.max_parts * a.head_groups;
-  const int grid = (int)(items < pkv::kGroupGridTarget ? (items > 0 ? items : 1)
-                                                        : pkv::kGroupGridTarget);
-  const hipError_t e = pkv::launch_pa_decode_grouped(a, D, grid, static_cast<hipStream_t>(stream));
+  const hipError_t e = pkv::launch_pa_decode_grouped(a, D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

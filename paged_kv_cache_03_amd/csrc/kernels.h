@@ -101,22 +101,17 @@ struct FlatArgs {
 };
 
 // Grouped decode (pa_decode_grouped.hip): groups of up to kGroupMaxMembers
-// sequences sharing leading blocks; one MFMA column per member.
+// sequences sharing leading blocks; one MFMA column per member; the groups'
+// positions lined up and cut into equal ranges.
 constexpr int kGroupMaxMembers = 16;
 constexpr int kGroupWaves = 4;             // waves (heads) per workgroup
 constexpr int kGroupTiles = 3;             // tiles in each wave's load ring
-constexpr int kMaxGroupPartBlocks = 64;    // longest partition, in positions (blocks)
-#ifndef PKV_GROUP_PART
-#define PKV_GROUP_PART 32
-#endif
 #ifndef PKV_GROUP_GRID
-#define PKV_GROUP_GRID 1024
+#define PKV_GROUP_GRID 512
 #endif
-constexpr int kGroupPartBlocks = PKV_GROUP_PART;   // partition length the launch plan asks for
-constexpr int kGroupGridTarget = PKV_GROUP_GRID;   // workgroups launched at most (grid-stride loop)
-constexpr int kGroupMaxLdsBytes = 48 * 1024;
-constexpr int kGroupItemCost = 8;          // an item's set-up, in positions (partition choice)
-constexpr int kGroupSlotsPerCU = 2;        // resident workgroups per CU (4 waves, <= 256 VGPRs)
+constexpr int kGroupGridTarget = PKV_GROUP_GRID;   // workgroups (ranges x head groups) at least
+constexpr int kGroupMaxLdsBytes = 44 * 1024;       // dynamic LDS: group offsets + range staging
+                                                   // (with the 16 KiB V staging: under 64 KiB)
 
 struct GroupArgs {
   const _Float16* q;
@@ -127,19 +122,20 @@ struct GroupArgs {
   const int32_t* group_offsets;  // [G + 1]: group g = sequences [off[g], off[g+1])
   const int32_t* group_shared;   // [G]: leading blocks the members share
   _Float16* out;
-  int* ws_map;         // [B][2]: first partition of the sequence's group, partitions*16 + member
-  float* ws_ml;        // [max_parts][group_size][H][2]: running max (log2 units), running sum
-  float* ws_acc;       // [max_parts][group_size][H][D]: unnormalised weighted sums
+  int* ws_map;         // [B]: group * 16 + member of each sequence, -1 if it is in no group
+  int* ws_gpos;        // [G + 1]: first position of each group, then the total
+  float* ws_ml;        // [H][nr][2 pieces][group_size][2]: running max (log2 units), sum
+  float* ws_acc;       // [H][nr][2 pieces][group_size][D]: unnormalised weighted sums
   float scale_log2;
   int B, H, G;
   int max_blocks;
   int ctx_limit;
   int num_blocks;
   int group_size;      // members decoded per group (1..kGroupMaxMembers)
-  int part_blocks;     // shortest partition length (positions) the workspace allows
-  int slots;           // workgroups resident at once (the rounds the items fill)
-  int max_parts;       // workspace capacity in partitions
   int head_groups;     // ceil(H / kGroupWaves)
+  int nr;              // ranges per head group
+  int max_chunk;       // longest range, in positions (LDS sizing)
+  int t_cap;           // positions the ranges can hold: nr * max_chunk (at most INT_MAX)
   bool keep_cached;
 };
 
@@ -198,8 +194,8 @@ hipError_t launch_hbm_read_probe(const void* buf, long long n16, uint32_t* sink,
                                  hipStream_t stream);
 hipError_t launch_hbm_gather_probe(const void* buf, const int32_t* order, long long n_chunks,
                                    int log_kib, uint32_t* sink, int grid, hipStream_t stream);
-hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, int grid, hipStream_t stream);
-size_t grouped_lds_bytes(int G);
+hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, hipStream_t stream);
+size_t grouped_lds_bytes(int G, int max_chunk);
 hipError_t launch_pa_prefill(const PrefillArgs& a, int D, int grid, int max_blocks_used,
                              hipStream_t stream);
 size_t prefill_lds_bytes(int B, int max_blocks_used);

@@ -264,13 +264,22 @@ def test_grouped_workspace_size():
     ws = lib.pkv_pa_decode_grouped_workspace_size
     assert ws(0, 32, 128, 2048, 0, 16) == 0
     assert ws(8, 32, 128, 2048, 3, 0) == 0 and ws(8, 32, 128, 2048, -1, 16) == 0
-    # grows with every dimension it depends on
+    # grows with every dimension it depends on: the batch (per-sequence
+    # map), members (partials per range), groups (offsets), and the context
+    # only once the ranges' LDS staging forces more ranges; the partials
+    # scale with heads x ranges, and the ranges per head group shrink as the
+    # head groups grow (the grid stays at its target)
     base = ws(200, 32, 128, 2048, 50, 4)
-    for bigger in (ws(400, 32, 128, 2048, 50, 4), ws(200, 64, 128, 2048, 50, 4),
-                   ws(200, 32, 128, 4096, 50, 4), ws(200, 32, 128, 2048, 50, 8),
-                   ws(200, 32, 128, 2048, 150, 4)):
+    for bigger in (ws(400, 32, 128, 2048, 50, 4), ws(200, 32, 128, 2048, 50, 8),
+                   ws(200, 32, 128, 2048, 150, 4), ws(4000, 32, 128, 1 << 16, 50, 4)):
         assert bigger > base
+    assert ws(200, 64, 128, 2048, 50, 4) == base
+    assert ws(200, 32, 128, 4096, 50, 4) == base
     assert ws(200, 32, 64, 2048, 50, 4) < base
+    # the group offsets are staged on chip next to at least one position of
+    # range staging: 11,259 groups are the most a call takes
+    assert ws(8, 32, 128, 2048, 11259, 16) > 0
+    assert ws(8, 32, 128, 2048, 11260, 16) == 0
 
 
 def test_prefill_rejects_bad_arguments(lib):
