@@ -213,31 +213,30 @@ void pa_prefill_kernel(PrefillArgs a) {
       const bool loader = wave * kWave < kLoaders;        // uniform per wave
       auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
       const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
+      // V token slots past the context must hold zeros (their weight is 0,
+      // and 0 times stale data could be NaN).  Only the last block can be
+      // partial: there the lanes of those tokens read past the resource,
+      // which returns zeros, so the staging copies every unit as loaded.
+      const int v_last = ctx - (nblk - 1) * kBlockTokens;   // valid tokens of the last block
+      const uint32_t v_off_last =
+          (int)((tid % kTileUnits) % kBlockTokens) < v_last ? unit_off : 0x7FFFFFF0u;
       auto fetch = [&](u4v (&r)[kUnits], int j) {
         const int jj = min(j, nblk - 1);
         const uint32_t bytes = j < nblk && loader ? kTile : 0u;
         const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
   #pragma unroll
-        for (int k = 0; k < kUnits; ++k)
-          r[k] = __builtin_amdgcn_raw_buffer_load_b128(
-              make_rsrc((unit_is_v(k) ? vbase : kbase) + o, bytes), unit_off, 0, 0);
-      };
-      auto stage = [&](const u4v (&r)[kUnits], int st, int j) {
-        const int valid = j < nblk ? min(kBlockTokens, ctx - j * kBlockTokens) : 0;
-        if (!loader) return;                              // uniform per wave
-  #pragma unroll
         for (int k = 0; k < kUnits; ++k) {
-          u4v w = r[k];
-          // a V unit holds 8 dims of token (tid % kTileUnits) % 16
-          const int u = tid % kTileUnits;
-          const bool is_v = unit_is_v(k);
-          const bool zero = is_v && u % kBlockTokens >= valid;
-          w.x = zero ? 0u : w.x;
-          w.y = zero ? 0u : w.y;
-          w.z = zero ? 0u : w.z;
-          w.w = zero ? 0u : w.w;
-          s_kv[st][is_v ? kTileUnits + v_slot(u) : u] = w;
+          const uint32_t off = unit_is_v(k) && j == nblk - 1 ? v_off_last : unit_off;
+          r[k] = __builtin_amdgcn_raw_buffer_load_b128(
+              make_rsrc((unit_is_v(k) ? vbase : kbase) + o, bytes), off, 0, 0);
         }
+      };
+      auto stage = [&](const u4v (&r)[kUnits], int st) {
+        if (!loader) return;                              // uniform per wave
+        const int u = tid % kTileUnits;
+  #pragma unroll
+        for (int k = 0; k < kUnits; ++k)
+          s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(u) : u] = r[k];
       };
       // transpose reads (offsets in halves inside a V tile): lane i = l%16 of
       // its 16-lane group addresses dims 8*g + 4*(i%2) .. +3 of token
@@ -357,34 +356,36 @@ void pa_prefill_kernel(PrefillArgs a) {
       u4v ring[R][kUnits];
   #pragma unroll
       for (int r = 0; r < R; ++r) fetch(ring[r], r);
-      stage(ring[0], 0, 0);
-      stage(ring[1], 1, 1);
+      stage(ring[0], 0);
+      stage(ring[1], 1);
       fetch(ring[0], 4);
       fetch(ring[1], 5);
       __syncthreads();
-      f16x16 sc_cur = {};
-      if (wave_rows) sc_cur = scores(0);
+      // The two halves of a round alternate the score registers (sc_a holds
+      // pair p's scores on entry), so no copy joins them.
+      f16x16 sc_a = {}, sc_b = {};
+      if (wave_rows) sc_a = scores(0);
       const int npairs = (nblk + 1) / 2;
       int sl = 0;                                         // pair slot of pair p
-      for (int p = 0; p < npairs; p += 2) {
-  #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int pn = p + u + 1;                       // the pair staged now
-          const int sn = sl == kSlots - 1 ? 0 : sl + 1;
-          const int ra = (2 * (u + 1)) % R;               // its ring tiles
-          stage(ring[ra], 2 * sn, 2 * pn);
-          fetch(ring[ra], 2 * pn + R);
-          stage(ring[ra + 1], 2 * sn + 1, 2 * pn + 1);
-          fetch(ring[ra + 1], 2 * pn + 1 + R);
-          __syncthreads();
-          if (wave_rows) {                                // uniform per wave
-            const float mref = prep(sc_cur, p + u);
-            const f16x16 sc_next = scores(sn);
-            weights_pv(sc_cur, mref, sl);
-            sc_cur = sc_next;
-          }
-          sl = sn;
+      auto half = [&](int p, int u, f16x16& cur, f16x16& next) {
+        const int pn = p + u + 1;                         // the pair staged now
+        const int sn = sl == kSlots - 1 ? 0 : sl + 1;
+        const int ra = (2 * (u + 1)) % R;                 // its ring tiles
+        stage(ring[ra], 2 * sn);
+        fetch(ring[ra], 2 * pn + R);
+        stage(ring[ra + 1], 2 * sn + 1);
+        fetch(ring[ra + 1], 2 * pn + 1 + R);
+        __syncthreads();
+        if (wave_rows) {                                  // uniform per wave
+          const float mref = prep(cur, p + u);
+          next = scores(sn);
+          weights_pv(cur, mref, sl);
         }
+        sl = sn;
+      };
+      for (int p = 0; p < npairs; p += 2) {
+        half(p, 0, sc_a, sc_b);
+        half(p, 1, sc_b, sc_a);
       }
     }
 
