@@ -60,6 +60,9 @@ def parse():
                          "the fused pa_decode_append")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the HBM read probes (achievable-bandwidth references)")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="one-layer workloads: calls timed after writing a 1 GiB scratch "
+                         "buffer, which evicts the L2 and the 256 MB MALL (0 = skip)")
     return ap.parse_args()
 
 
@@ -704,6 +707,26 @@ def main():
             achieved=round(unique_call / dec_avg_s / 1e9, 2),
             frac=round(unique_call / dec_avg_s / 1e9 / HBM_PEAK_GBS, 4),
             bytes_per_launch=int(unique_call), logical_bytes_per_launch=run.algo_bytes)
+
+    if args.cold_reps > 0 and args.workload in ("batch200", "batch10", "shared_prefix",
+                                                "vattention", "prefill_prompt",
+                                                "prefill_chunked"):
+        # The timed steps above run warm: a working set under 256 MB (batch 10)
+        # or shared blocks (the prefix) can be served by the MALL between
+        # steps.  Here every call starts after 1 GiB of unrelated writes.
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(args.cold_reps):
+            scratch.fill_(i & 0xFF)
+            ev = []
+            run.step(ev)
+            torch.cuda.synchronize()
+            cold.append(ev[0].elapsed_time(ev[1]))
+        del scratch
+        key = "pa_prefill" if pf is not None else "pa_decode"
+        result[key + "_us_cold_median"] = round(float(np.median(cold)) * 1e3, 3)
+        result[key + "_us_cold_p90"] = round(float(np.percentile(cold, 90)) * 1e3, 3)
+        result[key + "_cold_reps"] = args.cold_reps
 
     if not args.no_hbm_probe and args.workload == "batch200":
         probe = hbm_probe(torch, dev)
