@@ -42,7 +42,8 @@ def parse():
                     help="batch200 (default): the headline one-layer batch of 200")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0,
-                    help="sequences in the oracle sample (0 = sized to ~15 s)")
+                    help="sequences (groups, for the grouped decode) in the oracle sample "
+                         "(0 = sized to about 15 s)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     ap.add_argument("--decode", choices=["auto", "flat", "grouped"], default="auto",
@@ -179,41 +180,78 @@ def write_traffic_record(fetch_csv, write_csv, workload="batch200_seed2_pa_decod
     print(json.dumps(rec))
 
 
-def cpu_baseline(case, kp, vp, torch, budget_s=15.0, nseq=0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def _sample_pools(tables, kp, vp, torch):
+    """The blocks a sample of table rows reads, copied to the host as compact
+    pools, and the rows renumbered into them."""
     import numpy as np
-    from oracle import paged_decode_ref
-    order = list(range(case.batch))
-    # pick a sample whose tokens are proportional to the budget; start small
-    sample = order[: (nseq or 16)]
-    ids = np.unique(case.block_tables[sample].reshape(-1))
+    ids = np.unique(tables.reshape(-1))
     ids = ids[ids >= 0]
-    remap = np.full(case.num_blocks, -1, dtype=np.int32)
+    remap = np.full(int(ids.max()) + 1 if ids.size else 1, -1, dtype=np.int32)
     remap[ids] = np.arange(len(ids), dtype=np.int32)
     idx = torch.from_numpy(ids.astype(np.int64)).to(kp.device)
     k_small = kp.index_select(0, idx).cpu().numpy()
     v_small = vp.index_select(0, idx).cpu().numpy()
-    tables = np.where(case.block_tables[sample] >= 0,
-                      remap[np.maximum(case.block_tables[sample], 0)], -1).astype(np.int32)
-    lens = case.context_lens[sample]
+    rows = np.where(tables >= 0, remap[np.maximum(tables, 0)], -1).astype(np.int32)
+    return k_small, v_small, rows
+
+
+def cpu_baseline(run, torch, budget_s=15.0, units=0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the first sequences (whole groups for the grouped decode; layer 0 of a
+    full step), grown until the oracle takes about ``budget_s`` seconds."""
+    import numpy as np
+
+    import workloads as wl
+    from oracle import grouped_decode_ref, paged_decode_ref, paged_prefill_ref
+    case = run.case
+    q_all = case.q[0] if case.q.ndim == 4 else case.q
+    H, D = case.num_heads, case.head_dim
+    prefill = getattr(run, "prefill", None) is not None
+    grouped = run.extra.get("decode") == "pa_decode_grouped"
+    if grouped:
+        offs, shared = wl.table_groups(case.block_tables, case.context_lens)
+        total = len(shared)
+        n = min(total, units or 1)
+        nseq = int(offs[n])
+        what = f"first {n} of {total} groups, {nseq} sequences"
+    else:
+        total = case.batch
+        nseq = min(total, units or (2 if prefill else 16))   # a prefill sequence costs more
+        n = nseq
+        what = f"first {nseq} of {total} sequences"
+    k_small, v_small, tables = _sample_pools(case.block_tables[:nseq], run.kp, run.vp, torch)
+    lens = case.context_lens[:nseq]
     w0, c0 = time.perf_counter(), time.process_time()
-    paged_decode_ref(case.q[sample], k_small, v_small, tables, lens, case.scale)
+    if prefill:
+        qs = case.query_start[:nseq + 1].astype(np.int64)
+        paged_prefill_ref(q_all[qs[0]:qs[-1]], k_small, v_small, tables, lens, qs - qs[0],
+                          case.scale)
+    elif grouped:
+        grouped_decode_ref(q_all[:nseq], k_small, v_small, tables, lens, offs[:n + 1],
+                           shared[:n], case.scale)
+    else:
+        paged_decode_ref(q_all[:nseq], k_small, v_small, tables, lens, case.scale)
     wall, cpu = time.perf_counter() - w0, time.process_time() - c0
-    if not nseq and wall < budget_s / 4 and len(sample) < case.batch:
-        # scale the sample up to roughly the budget, within the batch
-        more = min(case.batch, int(len(sample) * budget_s / max(wall, 1e-3)))
-        return cpu_baseline(case, kp, vp, torch, budget_s, nseq=max(more, len(sample) + 1))
+    if not units and wall < budget_s / 4 and n < total:
+        # scale the sample up to roughly the budget, within the workload
+        more = min(total, int(n * budget_s / max(wall, 1e-3)))
+        return cpu_baseline(run, torch, budget_s, units=max(more, n + 1))
     tokens = int(lens.astype(np.int64).sum())
-    kv_bytes = tokens * 2 * case.num_heads * case.head_dim * 2
-    return {
-        "value": kv_bytes / wall / 1e9,
-        "unit": "GB/s",
-        "seq_layers_per_s": len(sample) / wall,
-        "cores": max(1, round(cpu / wall)),
-        "kind": "oracle",
-        "sample": f"first {len(sample)} of {case.batch} sequences ({tokens} context tokens), "
-                  f"one layer, float64 numpy oracle, {wall:.1f} s wall",
-    }
+    rec = {"cores": max(1, round(cpu / wall)), "kind": "oracle"}
+    layer = ", layer 0 of the step" if case.q.ndim == 4 else ", one layer"
+    if prefill:
+        rows = int(case.query_start[nseq] - case.query_start[0])
+        rec.update(value=rows / wall, unit="tokens/s",
+                   sample=f"{what} ({rows} query rows over {tokens} context tokens){layer}, "
+                          f"float64 numpy oracle, {wall:.1f} s wall")
+    else:
+        rec.update(value=tokens * 2 * H * D * 2 / wall / 1e9, unit="GB/s",
+                   seq_layers_per_s=nseq / wall,
+                   sample=f"{what} ({tokens} context tokens){layer}, float64 numpy oracle"
+                          + (" under the grouping contract" if grouped else "")
+                          + f", {wall:.1f} s wall")
+    return {k: rec[k] for k in ("value", "unit", "cores", "kind", "sample")} | \
+        {k: v for k, v in rec.items() if k not in ("value", "unit", "cores", "kind", "sample")}
 
 
 class Run:
@@ -751,9 +789,9 @@ def main():
                                 "gbs_read_plus_write": round(2 * n / t / 1e9, 1)}
         del src, dst
 
-    if not args.no_cpu_baseline and args.workload == "batch200":
+    if not args.no_cpu_baseline:
         log("timing the oracle on a sample of the workload (cpu baseline)")
-        result["cpu_baseline"] = cpu_baseline(run.case, run.kp, run.vp, torch, nseq=args.cpu_seqs)
+        result["cpu_baseline"] = cpu_baseline(run, torch, units=args.cpu_seqs)
         log(f"cpu baseline: {result['cpu_baseline']['sample']}")
     print(json.dumps(result), flush=True)
 
