@@ -96,11 +96,11 @@ bool decode_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx) {
          (long long)B * H <= (1LL << 26);
 }
 
-// Grouped decode: workspace = per-sequence map, then (m, l) and acc of every
-// (partition, member slot, head).  Partitions are bounded without looking at
-// device data: a group's partitions number at most its positions / part + 1,
-// and its positions at most the blocks of its members, so all groups together
-// have at most ceil(B * max_blocks / part) + G partitions.
+// Grouped decode: workspace = per-sequence map (group, member), the groups'
+// first positions, then (m, l) and acc of every (head, range, piece, member
+// slot).  The ranges are sized without looking at device data: all groups
+// together have at most B * ceil(max_ctx / 16) positions (a group's are at
+// most its members' blocks), cut into nr ranges of at most max_chunk.
 struct GroupPlan {
   int32_t nr = 0;          // ranges per head group
   int32_t max_chunk = 0;   // longest range, in positions
