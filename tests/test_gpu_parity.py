@@ -91,6 +91,18 @@ def test_edge_contexts(H, D, partition):
     assert not to_host(out)[0].any()          # empty context -> zero row
 
 
+@pytest.mark.parametrize("partition", [0, 512])
+def test_long_contexts(partition):
+    """Contexts far past the 2,048-token workloads (65,543 and 40,000
+    tokens: thousands of blocks per sequence, ranges and partitions that
+    stage hundreds of block ids) next to tiny and empty ones."""
+    c = _edge_case(4, 64, [65543, 3, 40000, 0], seed=91 + partition)
+    kp, vp = device_pools(c)
+    out = run_decode(c, kp, vp, partition=partition)
+    assert_close(out, oracle(c, c.k_pool, c.v_pool), f"long contexts part={partition}")
+    assert not to_host(out)[3].any()
+
+
 def test_batch10():
     c = wl.gpt_batch(10, seed=1)
     kp, vp = device_pools(c)

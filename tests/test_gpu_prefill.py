@@ -64,6 +64,18 @@ def test_ragged_prompts_and_chunks(H, D):
     assert zero.sum() == 3 and not to_host(out)[zero].any()
 
 
+def test_long_contexts():
+    """Contexts past 256 blocks (more block ids than threads to stage them
+    in one pass): a 200-row chunk over 4,800 cached tokens, one query at
+    the end of 4,200, and a whole 300-token prompt."""
+    lens = [5000, 4200, 300]
+    nq = [200, 1, 300]
+    q, kp, vp, tables, lens, qs = _ragged(77, 4, 64, lens, nq)
+    scale = float(np.float32(64 ** -0.5))
+    out = run_prefill(q, to_dev(kp), to_dev(vp), tables, lens, qs, scale, int(lens.max()))
+    assert_close(out, paged_prefill_ref(q, kp, vp, tables, lens, qs, scale), "long prefill")
+
+
 @pytest.mark.parametrize("mult", [1.0, -1.0, 0.0, 4.0])
 def test_scale_sign_zero_and_rising_scores(mult):
     """Keys that grow along the sequence (scores rise, so the online
