@@ -57,8 +57,8 @@ def parse():
                          "CSVs (FETCH_SIZE pass, WRITE_SIZE pass; both runs with --copy-probe) "
                          "and exit; needs no GPU")
     ap.add_argument("--separate-append", action="store_true",
-                    help="batch workloads: kv_append then pa_decode (two launches) instead of "
-                         "the fused pa_decode_append")
+                    help="batch and full-step workloads: kv_append then pa_decode (two "
+                         "launches) instead of the fused pa_decode_append")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the HBM read probes (achievable-bandwidth references)")
     ap.add_argument("--cold-reps", type=int, default=10,
@@ -387,7 +387,8 @@ def setup_full_step(torch, dev, wl, args, beams):
     """32 layers x 200 sequences x 2048 tokens; per step (beam groups:
     copy-on-write of each beam's last block in every layer, then) per layer
     append one token per sequence and decode."""
-    from paged_kv_cache_03_amd import cow_copy_blocks, kv_append, pa_decode, pa_decode_workspace_size
+    from paged_kv_cache_03_amd import (cow_copy_blocks, kv_append, pa_decode, pa_decode_append,
+                                       pa_decode_workspace_size)
     case = wl.full_step(beams=beams)
     B, H, D, L = case.batch, case.num_heads, case.head_dim, case.num_layers
     per_pool = case.num_blocks * H * 16 * D * 2
@@ -408,9 +409,15 @@ def setup_full_step(torch, dev, wl, args, beams):
     kv_layer, algo_layer = algorithmic_bytes(case.context_lens, H, D)
     layer_pools = [pools[l % distinct] for l in range(L)]
     grouped = beams > 1 and args.decode != "flat" or args.decode == "grouped"
+    # the single-query decode takes each layer's append in the same call
+    # (pa_decode_append), as the headline step does
+    fused = not grouped and not args.partition and not args.separate_append
     if grouped:
         decode, info = grouped_decoder(torch, dev, wl, case, 2048)
         dec_extra = {"decode": "pa_decode_grouped", **info}
+    elif fused:
+        dec_extra = {"decode": "pa_decode_append", "keep_cached": beams > 1}
+        algo_layer += 2 * (2 * B * H * D * 2)          # new rows read and written
     else:
         def decode(q, kp, vp, tables, lens, out):
             pa_decode(q, kp, vp, tables, lens, case.scale, out, max_context_len=2048,
@@ -422,23 +429,31 @@ def setup_full_step(torch, dev, wl, args, beams):
             cow_copy_blocks(pairs, [p[0] for p in pools], [p[1] for p in pools])
         for l in range(L):
             kp, vp = layer_pools[l]
-            kv_append(kn[l], vn[l], slots, kp, vp)
-            events.append(torch.cuda.Event(enable_timing=True))
-            events[-1].record()
-            decode(qs[l], kp, vp, tables, lens, out)
+            if fused:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+                pa_decode_append(qs[l], kn[l], vn[l], kp, vp, tables, lens, case.scale, out,
+                                 max_context_len=2048, workspace=ws, keep_cached=beams > 1)
+            else:
+                kv_append(kn[l], vn[l], slots, kp, vp)
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+                decode(qs[l], kp, vp, tables, lens, out)
             events.append(torch.cuda.Event(enable_timing=True))
             events[-1].record()
 
     import numpy as np
     used = np.unique(case.block_tables)
     return Run(case=case, kp=pools[0][0], vp=pools[0][1], step=step, seqs_per_step=B * L,
-               kv_bytes=kv_layer * L, algo_bytes=algo_layer,
+               kv_bytes=kv_layer * L, algo_bytes=algo_layer, fused=fused,
                strategy="grouped" if grouped else "flat" if not args.partition else "partitioned",
                part=args.partition,
                extra={"layers": L, "distinct_layer_pools": distinct, **dec_extra,
                       "unique_kv_bytes": int(used.size) * H * 16 * D * 2 * 2},
                config={"workload": f"full decode step: {L} layers x batch {B} x 2048 tokens, "
-                                   "32 heads x 128 dims fp16; per layer kv_append + decode"
+                                   "32 heads x 128 dims fp16; per layer "
+                                   + ("append fused into the decode (pa_decode_append)"
+                                      if fused else "kv_append + decode")
                                    + (f"; {beams}-beam groups sharing all but the last block, "
                                       "copy-on-write of the last block per beam" if beams > 1
                                       else ""),

@@ -12,7 +12,7 @@ import torch
 
 import workloads as wl
 from oracle import append_ref, paged_decode_ref
-from paged_kv_cache_03_amd import kv_append, pa_decode, pa_decode_append
+from paged_kv_cache_03_amd import cow_copy_blocks, kv_append, pa_decode, pa_decode_append
 from tests._gpu import assert_close, device_pools, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -104,6 +104,26 @@ def test_batch200_fused_equals_separate():
     seqs = list(range(0, 200, 17)) + [199]
     ref = paged_decode_ref(c.q, k_ref, v_ref, c.block_tables, c.context_lens, c.scale, seqs=seqs)
     assert_close(out2, ref, "fused append + decode, batch 200")
+
+
+@pytest.mark.parametrize("beams", [1, 4])
+def test_full_step_layer_fused_equals_separate(beams):
+    """One layer of the full step (200 sequences x 2048 tokens x 32 heads x
+    128; with 4 beams, after the copy-on-write of each beam's last block,
+    with the normal cache policy): fused and separate bit for bit."""
+    c = wl.full_step(layers=1, beams=beams)
+    torch.cuda.empty_cache()
+    kp, vp = device_pools(c, 0)
+    if c.cow_pairs is not None:
+        cow_copy_blocks(to_dev(c.cow_pairs), [kp], [vp])
+    (kp1, vp1, out1), (kp2, vp2, out2), slots = _both_ways(
+        c.q[0], c.k_new[0], c.v_new[0], kp, vp, c.block_tables, c.context_lens, c.scale, 2048,
+        keep_cached=beams > 1)
+    assert np.array_equal(slots, c.slot_mapping)
+    assert torch.equal(_bits(kp1), _bits(kp2)) and torch.equal(_bits(vp1), _bits(vp2))
+    assert torch.equal(out1, out2)
+    del kp1, vp1, kp2, vp2
+    torch.cuda.empty_cache()
 
 
 def test_repeated_steps_grow_the_cache():
