@@ -1,0 +1,164 @@
+"""Seeded random shapes through every decode entry point and the prefill,
+against the float64 oracle.
+
+Batch sizes, head counts (1-, 2- and 4-wave workgroups), head dims, context
+mixes (empty, one token, block edges, a few thousand tokens), partition
+lengths, cache policies and groupings are drawn from fixed seeds, so every
+run checks the same cases.  Slots no query may read hold NaN."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import append_ref, grouped_decode_ref, paged_decode_ref, paged_prefill_ref
+from paged_kv_cache_03_amd import pa_decode, pa_decode_append, pa_decode_grouped, pa_prefill
+from tests._gpu import assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [0, 1, 15, 16, 17, 31, 32, 33, 255, 256, 257]
+BUDGET = 3e7          # context tokens x H x D per case, so the oracle stays quick
+
+
+def _lens(rng, B, max_len):
+    """Context lengths: edge values and uniform draws, mixed."""
+    edge = rng.choice(EDGE_LENS, B)
+    draw = rng.integers(0, max_len + 1, B)
+    return np.minimum(np.where(rng.random(B) < 0.35, edge, draw), max_len).astype(np.int32)
+
+
+def _tables(rng, lens, extra_cols, shared=None):
+    """Block tables over a shuffled pool; ``shared`` maps a sequence to
+    (leader, blocks) whose first blocks it reuses."""
+    nblk = [-(-int(n) // 16) for n in lens]
+    NB = sum(nblk) + int(rng.integers(1, 6))
+    ids = list(rng.permutation(NB).astype(np.int32))
+    width = max(max(nblk), 1) + extra_cols
+    tables = np.full((len(lens), width), -1, dtype=np.int32)
+    for b, nb in enumerate(nblk):
+        lead, s = (shared or {}).get(b, (None, 0))
+        for j in range(nb):
+            tables[b, j] = tables[lead, j] if j < s else ids.pop()
+    return tables, NB
+
+
+def _case(rng, B, H, D, lens, tables, NB):
+    c = wl.Case("random", H, D, NB, lens, tables, wl.normal_fp16(rng, (B, H, D)),
+                float(np.float32(D ** -0.5)), wl.normal_fp16(rng, wl.pool_shape(NB, H, D)),
+                wl.normal_fp16(rng, wl.pool_shape(NB, H, D)))
+    return wl.poison_unused(c)
+
+
+def _decode_params(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 65))
+    H = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 32]))
+    D = int(rng.choice([64, 128]))
+    max_len = int(rng.choice([16, 100, 700, 3000]))
+    part = int(rng.choice([0, 0, 0, 16, 64, 256, 512]))
+    keep = bool(rng.integers(0, 2))
+    B = max(1, min(B, int(BUDGET // (max_len * H * D))))   # keeps the oracle quick
+    return rng, B, H, D, max_len, part, keep
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode(seed):
+    rng, B, H, D, max_len, part, keep = _decode_params(1000 + seed)
+    lens = _lens(rng, B, max_len)
+    tables, NB = _tables(rng, lens, int(rng.integers(0, 3)))
+    c = _case(rng, B, H, D, lens, tables, NB)
+    what = f"seed={seed} B={B} H={H} D={D} max_len={max_len} part={part} keep={keep}"
+    print(what, flush=True)
+    hint = min(max_len, 16 * tables.shape[1])           # at least the longest context
+    out = pa_decode(to_dev(c.q), to_dev(c.k_pool), to_dev(c.v_pool), to_dev(tables), to_dev(lens),
+                    c.scale, max_context_len=hint, partition_tokens=part, keep_cached=keep)
+    torch.cuda.synchronize()
+    assert_close(out, paged_decode_ref(c.q, c.k_pool, c.v_pool, tables, lens, c.scale), what)
+    assert not to_host(out)[lens == 0].any()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_fused_append(seed):
+    rng, B, H, D, max_len, _, keep = _decode_params(2000 + seed)
+    lens = _lens(rng, B, max_len)
+    tables, NB = _tables(rng, lens, 0)
+    c = _case(rng, B, H, D, lens, tables, NB)
+    k_new = wl.normal_fp16(rng, (B, H, D))
+    v_new = wl.normal_fp16(rng, (B, H, D))
+    slots = np.array([tables[b, (n - 1) // 16] * 16 + (n - 1) % 16 if n > 0 else -1
+                      for b, n in enumerate(lens)], dtype=np.int32)
+    what = f"seed={seed} B={B} H={H} D={D} max_len={max_len} keep={keep}"
+    print(what, flush=True)
+    kp, vp = to_dev(c.k_pool), to_dev(c.v_pool)
+    hint = min(max_len, 16 * tables.shape[1])           # at least the longest context
+    out = pa_decode_append(to_dev(c.q), to_dev(k_new), to_dev(v_new), kp, vp, to_dev(tables),
+                           to_dev(lens), c.scale, max_context_len=hint, keep_cached=keep)
+    torch.cuda.synchronize()
+    k_ref, v_ref = append_ref(k_new, v_new, slots, c.k_pool, c.v_pool)
+    assert np.array_equal(to_host(kp).view(np.int16), k_ref.view(np.int16))
+    assert np.array_equal(to_host(vp).view(np.int16), v_ref.view(np.int16))
+    assert_close(out, paged_decode_ref(c.q, k_ref, v_ref, tables, lens, c.scale), what)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_grouped(seed):
+    rng = np.random.default_rng(3000 + seed)
+    H = int(rng.choice([1, 2, 4, 6, 8, 32]))
+    D = int(rng.choice([64, 128]))
+    group_size = int(rng.choice([1, 3, 8, 16]))
+    if 120 * 840 * H * D > 4 * BUDGET:
+        H, D = 4, 64
+    # groups of 1..20 members (members past group_size get zero rows), a
+    # common prefix of P full blocks, then private tails
+    sizes = rng.integers(1, 21, int(rng.integers(1, 7)))
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    B = int(offs[-1])
+    lens = np.zeros(B, dtype=np.int32)
+    shared_blocks = np.zeros(len(sizes), dtype=np.int32)
+    share = {}
+    for g, (lo, hi) in enumerate(zip(offs[:-1], offs[1:])):
+        P = int(rng.integers(0, 40))
+        lens[lo:hi] = P * 16 + rng.integers(0, 200, hi - lo)
+        shared_blocks[g] = P + int(rng.integers(-1, 3))      # the contract clamps it
+        for b in range(lo + 1, hi):
+            share[b] = (int(lo), P)
+    tables, NB = _tables(rng, lens, 1, share)
+    c = _case(rng, B, H, D, lens, tables, NB)
+    max_len = int(lens.max())
+    what = f"seed={seed} B={B} G={len(sizes)} H={H} D={D} group_size={group_size}"
+    print(what, flush=True)
+    out = pa_decode_grouped(to_dev(c.q), to_dev(c.k_pool), to_dev(c.v_pool), to_dev(tables),
+                            to_dev(lens), to_dev(offs), to_dev(shared_blocks), c.scale,
+                            max_context_len=max_len, group_size=group_size)
+    torch.cuda.synchronize()
+    ref = grouped_decode_ref(c.q, c.k_pool, c.v_pool, tables, lens, offs, shared_blocks, c.scale,
+                             max_group_size=group_size)
+    assert_close(out, ref, what)
+    assert not to_host(out)[~ref.any(axis=(1, 2))].any()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_prefill(seed):
+    rng = np.random.default_rng(4000 + seed)
+    B = int(rng.integers(1, 17))
+    H = int(rng.choice([1, 2, 4, 6, 32]))
+    D = int(rng.choice([64, 128]))
+    if H == 32:
+        B, D = min(B, 4), 64
+    lens = _lens(rng, B, int(rng.choice([40, 300, 700])))
+    # queries: the whole context, a chunk of it, one row, or more rows than tokens
+    nq = np.array([min(int(n), int(rng.integers(0, 160))) if rng.random() < 0.8
+                   else int(n) + int(rng.integers(0, 5)) for n in lens], dtype=np.int32)
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    tables, NB = _tables(rng, lens, int(rng.integers(0, 2)))
+    c = _case(rng, B, H, D, lens, tables, NB)
+    q = wl.normal_fp16(rng, (max(int(qs[-1]), 1), H, D))[:int(qs[-1])]
+    what = f"seed={seed} B={B} H={H} D={D} rows={int(qs[-1])}"
+    print(what, flush=True)
+    if qs[-1] == 0:
+        return
+    out = pa_prefill(to_dev(q), to_dev(c.k_pool), to_dev(c.v_pool), to_dev(tables), to_dev(lens),
+                     to_dev(qs), c.scale, max_context_len=int(max(lens.max(), 1)))
+    torch.cuda.synchronize()
+    assert_close(out, paged_prefill_ref(q, c.k_pool, c.v_pool, tables, lens, qs, c.scale), what)
