@@ -1,5 +1,5 @@
-"""Seeded random shapes through every decode entry point and the prefill,
-against the float64 oracle.
+"""Seeded random shapes through every entry point (the decodes, the
+prefill, the append and the copy-on-write), against the oracle.
 
 Batch sizes, head counts (1-, 2- and 4-wave workgroups), head dims, context
 mixes (empty, one token, block edges, a few thousand tokens), partition
@@ -11,8 +11,9 @@ import pytest
 import torch
 
 import workloads as wl
-from oracle import append_ref, grouped_decode_ref, paged_decode_ref, paged_prefill_ref
-from paged_kv_cache_03_amd import pa_decode, pa_decode_append, pa_decode_grouped, pa_prefill
+from oracle import append_ref, cow_ref, grouped_decode_ref, paged_decode_ref, paged_prefill_ref
+from paged_kv_cache_03_amd import (cow_copy_blocks, kv_append, pa_decode, pa_decode_append,
+                                   pa_decode_grouped, pa_prefill)
 from tests._gpu import assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -162,3 +163,54 @@ def test_random_prefill(seed):
                      to_dev(qs), c.scale, max_context_len=int(max(lens.max(), 1)))
     torch.cuda.synchronize()
     assert_close(out, paged_prefill_ref(q, c.k_pool, c.v_pool, tables, lens, qs, c.scale), what)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_append(seed):
+    """Random distinct slots (some negative: skipped) over a random pool,
+    one to a few thousand tokens (both thread mappings of the append)."""
+    rng = np.random.default_rng(5000 + seed)
+    H = int(rng.choice([1, 3, 8, 32]))
+    D = int(rng.choice([64, 128]))
+    NB = int(rng.integers(1, 400))
+    T = int(min(rng.choice([1, 7, 200, 1500, 3000]), NB * 16))
+    slots = rng.choice(NB * 16, T, replace=False).astype(np.int32)
+    slots[rng.random(T) < 0.1] = -1
+    k = wl.normal_fp16(rng, (T, H, D))
+    v = wl.normal_fp16(rng, (T, H, D))
+    kp = wl.normal_fp16(rng, wl.pool_shape(NB, H, D))
+    vp = wl.normal_fp16(rng, wl.pool_shape(NB, H, D))
+    print(f"seed={seed} T={T} NB={NB} H={H} D={D}", flush=True)
+    kp_d, vp_d = to_dev(kp), to_dev(vp)
+    kv_append(to_dev(k), to_dev(v), to_dev(slots), kp_d, vp_d)
+    torch.cuda.synchronize()
+    k_ref, v_ref = append_ref(k, v, slots, kp, vp)
+    assert np.array_equal(to_host(kp_d).view(np.int16), k_ref.view(np.int16))
+    assert np.array_equal(to_host(vp_d).view(np.int16), v_ref.view(np.int16))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_copy_on_write(seed):
+    """Random conflict-free (src, dst) pairs, some with ids out of range
+    (skipped), over 1 to 40 layers (more than one launch past 32)."""
+    rng = np.random.default_rng(6000 + seed)
+    H = int(rng.choice([1, 4, 32]))
+    D = int(rng.choice([64, 128]))
+    NB = int(rng.integers(4, 120))
+    L = int(rng.choice([1, 2, 33, 40]))
+    n = int(rng.integers(1, NB // 2 + 1))
+    perm = rng.permutation(NB).astype(np.int32)
+    pairs = np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32)
+    bad = rng.random(n) < 0.15
+    pairs[bad, rng.integers(0, 2, n)[bad]] = NB + 3
+    pools = [(wl.normal_fp16(rng, wl.pool_shape(NB, H, D)),
+              wl.normal_fp16(rng, wl.pool_shape(NB, H, D))) for _ in range(L)]
+    print(f"seed={seed} pairs={n} NB={NB} layers={L} H={H} D={D}", flush=True)
+    dev_pools = [(to_dev(k), to_dev(v)) for k, v in pools]
+    cow_copy_blocks(to_dev(pairs), [p[0] for p in dev_pools], [p[1] for p in dev_pools])
+    torch.cuda.synchronize()
+    keep = (pairs >= 0).all(axis=1) & (pairs < NB).all(axis=1)
+    ref = cow_ref([x for p in pools for x in p], pairs[keep])
+    got = [to_host(x) for p in dev_pools for x in p]
+    for r, g in zip(ref, got):
+        assert np.array_equal(r.view(np.int16), g.view(np.int16))
