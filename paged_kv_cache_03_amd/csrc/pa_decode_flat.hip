@@ -6,13 +6,17 @@
 //
 //  * For one head, line up every block of every sequence, sequence after
 //    sequence: positions 0 .. T-1, with sequence b owning [S_b, S_{b+1}).
-//  * The grid is sized to what the GPU holds at once.  Workgroup i serves
-//    head group i % G (so, with G == 8, one XCD per head group and shared
-//    blocks found in that XCD's L2) and takes the i / G-th of NR equal,
-//    contiguous ranges of positions.  Every wave of the workgroup (one per
-//    head) streams through the whole range: no wave starts over at a
-//    partition boundary, and the ranges differ in length by at most one
-//    block.
+//  * The grid is sized to what the GPU holds at once.  Each workgroup serves
+//    one head group and one of NR equal, contiguous ranges of positions.
+//    Workgroup i runs on XCD i % 8.  When blocks are shared between
+//    sequences (the normal cache policy), workgroup i serves head group
+//    i % G and range i / G, so a head group stays on one XCD (with G == 8)
+//    and its shared blocks are found in that XCD's L2.  When tiles stream
+//    (non-temporal), each XCD serves every head group and every eighth
+//    range, which spreads each XCD's reads over the whole pool (1% faster
+//    at batch 200).  Every wave of the workgroup (one per head) streams
+//    through the whole range: no wave starts over at a partition boundary,
+//    and the ranges differ in length by at most one block.
 //  * A wave keeps a ring of kFlatTiles tiles in registers: while it works
 //    on one block the next ones are in flight.  The prefetch runs straight
 //    across sequence boundaries.
@@ -165,8 +169,12 @@ __global__ __launch_bounds__(64 * kFlatMaxWaves) void pa_decode_flat_kernel(Flat
   const int lane = tid % kWave;
   const int token = lane % kBlockTokens;
   const int row = lane / kBlockTokens;
-  const int g = blockIdx.x % a.head_groups;
-  const int r = blockIdx.x / a.head_groups;
+  // workgroup -> (head group g, range r); both mappings are one-to-one
+  // over the grid (head_groups * nr workgroups)
+  const bool spread = kPolicy == kStreamPolicy && a.nr % 8 == 0;
+  const int g = spread ? (blockIdx.x / 8) % a.head_groups : blockIdx.x % a.head_groups;
+  const int r = spread ? (blockIdx.x / 8 / a.head_groups) * 8 + blockIdx.x % 8
+                       : blockIdx.x / a.head_groups;
   const int h = g * a.waves_per_group + wave;
 
   block_prefix(a.context_lens, kContig ? a.capacity : nullptr, a.B, a.ctx_limit, s_start, s_tail,
