@@ -8,8 +8,8 @@ one layer of a GPT-style model, batch 200, 32 heads x 128 dims, fp16,
 capped at 2048, pool = blocks needed + 10% free, tables from a shuffled free
 list (seed 2).  Inputs are resident in HBM before the timed region.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
-GPU.
+Prints one JSON line.  ``--gpus`` above 1 is refused: the library runs on
+one GPU (there is no multi-GPU path).
 """
 
 import argparse
@@ -639,8 +639,8 @@ def main():
         write_traffic_record(*args.traffic_from)
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
-              "(every GPU box here has one).", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported; the library runs on one GPU "
+              "(there is no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -14,7 +14,7 @@ Sources:
   newly allocated page (copy-on-write at block granularity); the other
   sharers keep pointing at the original, which is left unchanged.
 
-Readings (listed in DESIGN.md): a slot is ``physical_block * 16 + position``;
+Readings where the pages are silent: a slot is ``physical_block * 16 + position``;
 a negative slot means "skip this row"; slots and copy pairs are free of
 conflicts (no slot twice, no destination that is also a source or a repeated
 destination), so the order in which the copies happen does not matter.

@@ -17,7 +17,7 @@ Sources, by page and section:
 * "Atención paginada en modelos de lenguaje grandes (LLM)" (7minutos.es),
   PagePool part: pages of 16 tokens each.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * the scale is supplied by the caller (the workloads pass 1/sqrt(D) as a
   float32); the oracle widens it to float64;

@@ -17,7 +17,7 @@ Sources, by page and section:
   as they are processed, so a prompt is written into its pages before (or
   while) it is attended to.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
 
 * a prefill call processes, for every sequence b, its last
   ``n_b = query_start[b+1] - query_start[b]`` cached tokens as queries (the

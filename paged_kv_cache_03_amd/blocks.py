@@ -18,7 +18,7 @@ Sources:
   blocks are reference counted and shared between requests or decoding
   branches, with block-granular copy-on-write.
 
-Readings (listed in the design doc): the owner of a shared prefix holds one
+Readings where the pages are silent: the owner of a shared prefix holds one
 reference; a copy happens only when a shared page is about to be written
 (a page held once is written in place); pool exhaustion raises
 ``PoolExhausted`` (no eviction); the free list hands pages out in ascending
