@@ -57,8 +57,12 @@ def parse():
                          "CSVs (FETCH_SIZE pass, WRITE_SIZE pass; both runs with --copy-probe) "
                          "and exit; needs no GPU")
     ap.add_argument("--separate-append", action="store_true",
-                    help="batch and full-step workloads: kv_append then pa_decode (two "
-                         "launches) instead of the fused pa_decode_append")
+                    help="batch, full-step and prefill workloads: kv_append then pa_decode "
+                         "or pa_prefill (two launches) instead of the fused pa_decode_append "
+                         "or pa_prefill_append")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="prefill_chunked: one pa_prefill_append call instead of kv_append "
+                         "then pa_prefill")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the HBM read probes (achievable-bandwidth references)")
     ap.add_argument("--cold-reps", type=int, default=10,
@@ -587,10 +591,13 @@ def setup_vattention(torch, dev, wl, args):
 
 def setup_prefill(torch, dev, wl, args, chunked):
     """One layer of prefill: per step the new tokens' keys and values are
-    appended through their slots, then every new token attends causally over
-    its sequence (pa_prefill).  Prompts: 200 sequences of U[32, 256] tokens;
-    chunked: 32 sequences, a 512-token chunk over 1536 cached tokens."""
-    from paged_kv_cache_03_amd import kv_append, pa_prefill
+    written to their slots and every new token attends causally over its
+    sequence.  Prompts: 200 sequences of U[32, 256] tokens, one
+    pa_prefill_append call (--separate-append: kv_append, then pa_prefill);
+    chunked: 32 sequences, a 512-token chunk over 1536 cached tokens,
+    kv_append then pa_prefill, the faster of the two there (--fused-append:
+    one pa_prefill_append call)."""
+    from paged_kv_cache_03_amd import kv_append, pa_prefill, pa_prefill_append
     import numpy as np
     case = wl.prefill(32, seed=7, cached=1536, chunk=512, fill=False) if chunked else \
         wl.prefill(fill=False)
@@ -603,11 +610,18 @@ def setup_prefill(torch, dev, wl, args, chunked):
     out = torch.empty_like(q)
     max_ctx = case.max_context
 
+    fused = args.fused_append if chunked else not args.separate_append
+
     def step(events):
-        kv_append(kn, vn, slots, kp, vp)
+        if not fused:
+            kv_append(kn, vn, slots, kp, vp)
         events.append(torch.cuda.Event(enable_timing=True))
         events[-1].record()
-        pa_prefill(q, kp, vp, tables, lens, qs, case.scale, out, max_context_len=max_ctx)
+        if fused:
+            pa_prefill_append(q, kn, vn, kp, vp, tables, lens, qs, case.scale, out,
+                              max_context_len=max_ctx)
+        else:
+            pa_prefill(q, kp, vp, tables, lens, qs, case.scale, out, max_context_len=max_ctx)
         events.append(torch.cuda.Event(enable_timing=True))
         events[-1].record()
 
@@ -618,15 +632,21 @@ def setup_prefill(torch, dev, wl, args, chunked):
     flops = 4 * H * D * pairs                          # q.k and p.v, 2 flops per multiply-add
     kv_bytes = int(ctx.sum()) * H * D * 2 * 2          # every cached token's K and V once
     io_bytes = int(n.sum()) * H * D * 2 * 2            # q read, out written
+    # fused: the new tokens' K and V are read from their rows instead of the
+    # pools (the same count) and written to the pools once
+    write_bytes = int(np.maximum(np.minimum(n, ctx), 0).sum()) * H * D * 2 * 2 if fused else 0
     rows = int(n.sum())
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=case.batch, kv_bytes=kv_bytes,
-               algo_bytes=kv_bytes + io_bytes, strategy="prefill", part=0,
-               prefill={"rows": rows, "flops": flops, "pairs": pairs},
+               algo_bytes=kv_bytes + io_bytes + write_bytes, strategy="prefill", part=0,
+               prefill={"rows": rows, "flops": flops, "pairs": pairs,
+                        "kernel": "pa_prefill_append" if fused else "pa_prefill"},
                extra={"query_rows": rows, "causal_pairs": pairs},
                config={"workload": ("one layer, 32 sequences x (1536 cached + 512-token chunk)"
                                     if chunked else "one layer, 200 prompts of U[32,256] tokens")
-                                   + ", 32 heads x 128 dims fp16; per step kv_append of the new "
-                                   "tokens + causal pa_prefill",
+                                   + ", 32 heads x 128 dims fp16; per step "
+                                   + ("pa_prefill_append (the new tokens written to their pages "
+                                      "and attended causally in one call)" if fused else
+                                      "kv_append of the new tokens + causal pa_prefill"),
                        "batch": case.batch, "heads": H, "head_dim": D, "block_tokens": 16,
                        "query_rows": rows, "context_tokens": case.kv_tokens(),
                        "max_context": max_ctx, "num_blocks": case.num_blocks,
@@ -744,12 +764,12 @@ def main():
         for k in ("pa_decode_kv_gbs", "pa_decode_pct_hbm_peak", "pct_hbm_peak"):
             result.pop(k, None)
         if t_mfma >= t_hbm:
-            result["roofline"].update(kernel="pa_prefill", bound="mfma", unit="TFLOP/s",
+            result["roofline"].update(kernel=pf["kernel"], bound="mfma", unit="TFLOP/s",
                                       achieved=round(tflops, 2), peak=MFMA_F16_PEAK_TFLOPS,
                                       frac=round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                                       flops_per_launch=pf["flops"])
         else:
-            result["roofline"].update(kernel="pa_prefill")
+            result["roofline"].update(kernel=pf["kernel"])
     if "unique_kv_bytes" in run.extra:      # per decode call: each distinct block once
         result["pa_decode_unique_kv_gbs"] = round(run.extra["unique_kv_bytes"] / dec_avg_s / 1e9, 2)
         # blocks shared by several sequences: HBM sees each once, so the

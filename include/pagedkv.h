@@ -306,6 +306,39 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                    void* stream);
 
 /*
+ * Prefill with its append fused in ("Atención paginada en modelos de
+ * lenguaje grandes (LLM)", 7minutos.es, PagePool / PagedRequest part: a
+ * request's tokens are written into its pages slot by slot as they are
+ * processed; "PagedAttention", e-fortepiano.pl, "Formulació matemàtica"):
+ * the same result as pkv_kv_append of the new rows followed by
+ * pkv_pa_prefill, in one call.  Row r = query_start[b] + i of k_new / v_new
+ * is the key / value of position p = context_lens[b] - n_b + i of sequence b
+ * (context_lens counts the new tokens); it is written to slot
+ * block_tables[b][p / 16] * 16 + p % 16 of both pools (rows at a negative
+ * position are not written), and the queries attend as for pkv_pa_prefill.
+ * Blocks whose tokens are all new are read from k_new / v_new rather than
+ * from the pools; the new tokens of a block that also holds cached tokens
+ * are written by a first, small kernel, so any split of a sequence into
+ * chunks is allowed.  Pools and out equal those of the two separate calls
+ * bit for bit.
+ *
+ * device: k_new, v_new [num_query_rows][H][D] fp16 (16-byte aligned), the
+ *         rest as for pkv_pa_prefill; k_pool and v_pool are written.
+ * host:   as for pkv_pa_prefill.  query_start must stay within
+ *         [0, num_query_rows]; otherwise the new tokens' slots and the
+ *         outputs are unspecified (no memory outside the buffers passed is
+ *         touched).  Errors as for pkv_pa_prefill, and PKV_ERR_NULL_PTR /
+ *         PKV_ERR_MISALIGNED for k_new and v_new.
+ */
+int pkv_pa_prefill_append(const void* q, const void* k_new, const void* v_new,
+                          void* k_pool, void* v_pool, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, const int32_t* query_start,
+                          int32_t num_query_rows, int32_t B, int32_t H, int32_t D,
+                          int32_t block_size, int32_t num_blocks, float scale, void* out,
+                          uint32_t flags, void* stream);
+
+/*
  * Contiguous KV cache in virtual memory, physical memory on demand: the
  * alternative to paging that "PagedAttention" (e-fortepiano.pl) describes in
  * "Limitacions i alternatives" and "Atenció" (vAttention).  Each layer's K

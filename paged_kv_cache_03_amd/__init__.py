@@ -17,4 +17,4 @@ from .ops import (VirtualKV, contig_decode, contig_decode_rows,  # noqa: F401
                   cow_copy_blocks, default_partition,
                   kv_append, pa_decode, pa_decode_append,
                   pa_decode_grouped, pa_decode_grouped_workspace_size, pa_decode_workspace_size,
-                  pa_prefill, pool_shape)
+                  pa_prefill, pa_prefill_append, pool_shape)

@@ -42,6 +42,9 @@ SIGNATURES = {
     "pkv_pa_decode_grouped_workspace_size": (_c.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_pa_prefill": (_c.c_int, [_vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32p, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _c.c_float, _vp, _c.c_uint32, _vp]),
+    "pkv_pa_prefill_append": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32p,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _c.c_float, _vp,
+                                         _c.c_uint32, _vp]),
     "pkv_contig_decode": (_c.c_int, [_vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i32, _i32,
                                      _c.c_float, _vp, _vp, _c.c_size_t, _c.c_uint32, _vp]),
     "pkv_contig_decode_workspace_size": (_c.c_size_t, [_i32, _i32, _i32, _i32]),

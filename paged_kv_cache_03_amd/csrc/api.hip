@@ -429,12 +429,16 @@ int pkv_pa_decode_grouped(const void* q, const void* k_pool, const void* v_pool,
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
-                   const int32_t* block_tables, int32_t max_blocks_per_seq,
-                   const int32_t* context_lens, int32_t max_context_len,
-                   const int32_t* query_start, int32_t num_query_rows, int32_t B, int32_t H,
-                   int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
-                   uint32_t flags, void* stream) {
+namespace {
+
+// pkv_pa_prefill and pkv_pa_prefill_append: k_new / v_new are null for the
+// former, the new tokens' rows for the latter.
+int prefill_call(const void* q, const void* k_new, const void* v_new, const void* k_pool,
+                 const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t max_context_len,
+                 const int32_t* query_start, int32_t num_query_rows, int32_t B, int32_t H,
+                 int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                 uint32_t flags, void* stream, bool append) {
   if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
   if (flags != 0) return PKV_ERR_BAD_SHAPE;
   if (!decode_shape_ok(B, H, D, max_context_len) || num_query_rows < 0 ||
@@ -450,10 +454,12 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   // query groups: sum over sequences of ceil(n_b / R) <= num_query_rows / R + B, R = kPrefillRows
   const long long bound = ((long long)ceil_div(num_query_rows, pkv::kPrefillRows) + B) * H;
   if (bound >= (1LL << 31)) return PKV_ERR_BAD_SHAPE;
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out)
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out ||
+      (append && (!k_new || !v_new)))
     return PKV_ERR_NULL_PTR;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
+      (append && (!aligned(k_new, 16) || !aligned(v_new, 16))))
     return PKV_ERR_MISALIGNED;
   pkv::PrefillArgs a;
   a.q = static_cast<const _Float16*>(q);
@@ -470,6 +476,8 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = max_context_len;
   a.num_blocks = num_blocks;
+  a.k_new = append ? static_cast<const _Float16*>(k_new) : nullptr;
+  a.v_new = append ? static_cast<const _Float16*>(v_new) : nullptr;
   // the items run in a grid-stride loop over at most eight workgroups per
   // resident slot: few enough that no workgroup is launched only to find no
   // item, enough that the hardware's dispatch still balances items of
@@ -481,9 +489,34 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
     return PKV_ERR_HIP;
   const long long resident = (long long)cus * pkv::kPrefillSlotsPerCU * 8 / 8 * 8;
   const int grid = (int)(bound < resident ? bound : (resident > 0 ? resident : bound));
-  const hipError_t e = pkv::launch_pa_prefill(a, D, grid, blocks_used,
-                                              static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      append ? pkv::launch_pa_prefill_append(a, D, grid, blocks_used, static_cast<hipStream_t>(stream))
+             : pkv::launch_pa_prefill(a, D, grid, blocks_used, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len,
+                   const int32_t* query_start, int32_t num_query_rows, int32_t B, int32_t H,
+                   int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
+                   uint32_t flags, void* stream) {
+  return prefill_call(q, nullptr, nullptr, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                      context_lens, max_context_len, query_start, num_query_rows, B, H, D,
+                      block_size, num_blocks, scale, out, flags, stream, false);
+}
+
+int pkv_pa_prefill_append(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len,
+                          const int32_t* query_start, int32_t num_query_rows, int32_t B,
+                          int32_t H, int32_t D, int32_t block_size, int32_t num_blocks,
+                          float scale, void* out, uint32_t flags, void* stream) {
+  return prefill_call(q, k_new, v_new, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                      context_lens, max_context_len, query_start, num_query_rows, B, H, D,
+                      block_size, num_blocks, scale, out, flags, stream, true);
 }
 
 int pkv_kv_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t T,

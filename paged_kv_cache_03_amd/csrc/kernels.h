@@ -162,6 +162,10 @@ struct PrefillArgs {
   int max_blocks;
   int ctx_limit;
   int num_blocks;
+  // the append fused into the prefill (pkv_pa_prefill_append): the new
+  // tokens' keys and values, [num_rows][H][D] like q; null otherwise
+  const _Float16* k_new;
+  const _Float16* v_new;
 };
 
 struct AppendArgs {
@@ -198,6 +202,8 @@ hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, hipStream_t strea
 size_t grouped_lds_bytes(int G, int max_chunk);
 hipError_t launch_pa_prefill(const PrefillArgs& a, int D, int grid, int max_blocks_used,
                              hipStream_t stream);
+hipError_t launch_pa_prefill_append(const PrefillArgs& a, int D, int grid, int max_blocks_used,
+                                    hipStream_t stream);
 size_t prefill_lds_bytes(int B, int max_blocks_used);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_cow_copy(const CowArgs& a, hipStream_t stream);

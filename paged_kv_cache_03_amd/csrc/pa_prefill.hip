@@ -114,7 +114,16 @@ __device__ __forceinline__ int seq_of_group(const int* s_group, int B, int t) {
 
 // Two waves per SIMD (two workgroups per CU): the register budget that
 // allows fits the kernel without spilling.
-template <int D>
+//
+// kAppend: the append of the new tokens is fused in.  Blocks whose tokens
+// are all new are read from the caller's rows (a.k_new / a.v_new) instead
+// of the pools; blocks with cached tokens (the one the new tokens start in
+// included, whose new tokens a separate kernel writes first) come from the
+// pools.  The source is one choice per tile, taken with selects, and the
+// item whose query rows hold a block's first token writes that block to
+// the pools as it stages it (a store with an empty range for the other
+// tiles), so the load ring keeps its fixed shape.
+template <int D, bool kAppend>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pa_prefill_kernel(PrefillArgs a) {
   typedef float f16x16 __attribute__((ext_vector_type(16)));
@@ -159,6 +168,10 @@ void pa_prefill_kernel(PrefillArgs a) {
     const int p_group = ctx - n + row0;                   // position of the group's first row
     const int p_last = min(p_group + grows - 1, ctx - 1);
     const int nblk = p_last >= 0 ? p_last / kBlockTokens + 1 : 0;
+    // fused append: position of the sequence's first new token, and the
+    // first block whose tokens are all new
+    const int bnd = ctx - n;
+    const int jn = kAppend ? (max(bnd, 0) + kBlockTokens - 1) / kBlockTokens : 0x7fffffff;
 
     for (int j = tid; j < nblk; j += blockDim.x) {
       const int id = a.block_tables[(size_t)b * a.max_blocks + j];
@@ -201,18 +214,41 @@ void pa_prefill_kernel(PrefillArgs a) {
   #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
 
+    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
+    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
+    const size_t block_stride = (size_t)a.H * kTile;
+    // The tile pair is 2 * kTileUnits 16-byte units; the first kLoaders
+    // threads load them, unit u = tid + kLoaders * k (K for u < kTileUnits,
+    // V after).  kTileUnits and kLoaders are multiples of 64, so the choice
+    // of K or V is uniform per wave and the buffer resource stays in scalar
+    // registers.
+    const bool loader = wave * kWave < kLoaders;        // uniform per wave
+    auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
+    const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
+    // Rows source (fused append): in a tile read from the caller's rows this
+    // thread's unit is token t_r, dims 8 g_r .. +7 (16 consecutive lanes read
+    // one token's row of the head, 2 D bytes), which is unit u_r of the
+    // pool's tile layout.  row_r is the row of token t_r of block 0.
+    const int ur = tid % kTileUnits;
+    const int t_r = ur / (D / 8);
+    const int g_r = ur % (D / 8);
+    const int u_r = g_r * kBlockTokens + t_r;
+    const int row_r = a.query_start[b] - bnd + t_r;
+    const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
+    const uint32_t rows_total = (uint32_t)a.num_rows * row_bytes;
+    // byte offset of token t_r of block 0 (modulo 2^32: row_r may be
+    // negative, the rows of the tokens that exist are not)
+    const uint32_t row_base = (uint32_t)row_r * row_bytes + (uint32_t)((h * D + 8 * g_r) * 2);
+    // Token t_r of block j exists if it lies inside the context; tiles at or
+    // past nblk read as zeros.  With query_start inside [0, num_rows] its row
+    // is one of the sequence's; the buffer bounds keep any other row inside
+    // the caller's rows.
+    auto row_off = [&](int j) {
+      return j < nblk && t_r < ctx - kBlockTokens * j
+                 ? row_base + (uint32_t)j * (uint32_t)kBlockTokens * row_bytes
+                 : 0xFFFFFFF0u;
+    };
     if (nblk > 0) {
-      const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
-      const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
-      const size_t block_stride = (size_t)a.H * kTile;
-      // The tile pair is 2 * kTileUnits 16-byte units; the first kLoaders
-      // threads load them, unit u = tid + kLoaders * k (K for u < kTileUnits,
-      // V after).  kTileUnits and kLoaders are multiples of 64, so the choice
-      // of K or V is uniform per wave and the buffer resource stays in scalar
-      // registers.
-      const bool loader = wave * kWave < kLoaders;        // uniform per wave
-      auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
-      const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
       // V token slots past the context must hold zeros (their weight is 0,
       // and 0 times stale data could be NaN).  Only the last block can be
       // partial: there the lanes of those tokens read past the resource,
@@ -220,23 +256,50 @@ void pa_prefill_kernel(PrefillArgs a) {
       const int v_last = ctx - (nblk - 1) * kBlockTokens;   // valid tokens of the last block
       const uint32_t v_off_last =
           (int)((tid % kTileUnits) % kBlockTokens) < v_last ? unit_off : 0x7FFFFFF0u;
-      auto fetch = [&](u4v (&r)[kUnits], int j) {
+      auto fetch = [&](u4v (&r)[kUnits], size_t& o, int j) {
         const int jj = min(j, nblk - 1);
         const uint32_t bytes = j < nblk && loader ? kTile : 0u;
-        const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
+        o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
+        const bool rows = kAppend && j >= jn;             // uniform
+        const uint32_t roff = kAppend ? row_off(j) : 0u;
   #pragma unroll
         for (int k = 0; k < kUnits; ++k) {
           const uint32_t off = unit_is_v(k) && j == nblk - 1 ? v_off_last : unit_off;
-          r[k] = __builtin_amdgcn_raw_buffer_load_b128(
-              make_rsrc((unit_is_v(k) ? vbase : kbase) + o, bytes), off, 0, 0);
+          const char* pool = (unit_is_v(k) ? vbase : kbase) + o;
+          if constexpr (kAppend) {
+            const char* src = rows ? reinterpret_cast<const char*>(unit_is_v(k) ? a.v_new : a.k_new)
+                                   : pool;
+            r[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                make_rsrc(src, rows ? rows_total : bytes), rows ? roff : off, 0, 0);
+          } else {
+            r[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(pool, bytes), off, 0, 0);
+          }
         }
       };
-      auto stage = [&](const u4v (&r)[kUnits], int st) {
+      // Stage block j's tiles (pool offset o) into pair slot half st (a tile
+      // read from the rows holds unit u_r where a pool tile holds unit u).
+      // With the append, a tile read from the rows also goes to its pool
+      // block when this item owns the block (its rows hold the block's first
+      // token): the store is issued for every tile, with an empty range when
+      // the item does not own it, so the ring's wait counts stay fixed.
+      auto stage = [&](const u4v (&r)[kUnits], int st, int j, size_t o) {
         if (!loader) return;                              // uniform per wave
         const int u = tid % kTileUnits;
+        const bool rows = kAppend && j >= jn;             // uniform
+        const int slot = rows ? u_r : u;
   #pragma unroll
         for (int k = 0; k < kUnits; ++k)
-          s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(u) : u] = r[k];
+          s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(slot) : slot] = r[k];
+        if constexpr (kAppend) {
+          const bool own = rows && j < nblk && (kBlockTokens * j - bnd) / kPrefillRows == kq;
+          const uint32_t woff = t_r < ctx - kBlockTokens * j ? (uint32_t)u_r * 16u : 0xFFFFFFF0u;
+  #pragma unroll
+          for (int k = 0; k < kUnits; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                r[k], make_rsrc(const_cast<char*>((unit_is_v(k) ? vbase : kbase) + o),
+                                own ? kTile : 0u),
+                woff, 0, 0);
+        }
       };
       // transpose reads (offsets in halves inside a V tile): lane i = l%16 of
       // its 16-lane group addresses dims 8*g + 4*(i%2) .. +3 of token
@@ -354,12 +417,13 @@ void pa_prefill_kernel(PrefillArgs a) {
       // the last block see valid = 0 (exact no-ops), so the loop runs whole
       // rounds of two pairs with no exit in its body.
       u4v ring[R][kUnits];
+      size_t ring_o[R];                                   // pool offsets of the ring's blocks
   #pragma unroll
-      for (int r = 0; r < R; ++r) fetch(ring[r], r);
-      stage(ring[0], 0);
-      stage(ring[1], 1);
-      fetch(ring[0], 4);
-      fetch(ring[1], 5);
+      for (int r = 0; r < R; ++r) fetch(ring[r], ring_o[r], r);
+      stage(ring[0], 0, 0, ring_o[0]);
+      stage(ring[1], 1, 1, ring_o[1]);
+      fetch(ring[0], ring_o[0], 4);
+      fetch(ring[1], ring_o[1], 5);
       __syncthreads();
       // The two halves of a round alternate the score registers (sc_a holds
       // pair p's scores on entry), so no copy joins them.
@@ -371,10 +435,10 @@ void pa_prefill_kernel(PrefillArgs a) {
         const int pn = p + u + 1;                         // the pair staged now
         const int sn = sl == kSlots - 1 ? 0 : sl + 1;
         const int ra = (2 * (u + 1)) % R;                 // its ring tiles
-        stage(ring[ra], 2 * sn);
-        fetch(ring[ra], 2 * pn + R);
-        stage(ring[ra + 1], 2 * sn + 1);
-        fetch(ring[ra + 1], 2 * pn + 1 + R);
+        stage(ring[ra], 2 * sn, 2 * pn, ring_o[ra]);
+        fetch(ring[ra], ring_o[ra], 2 * pn + R);
+        stage(ring[ra + 1], 2 * sn + 1, 2 * pn + 1, ring_o[ra + 1]);
+        fetch(ring[ra + 1], ring_o[ra + 1], 2 * pn + 1 + R);
         __syncthreads();
         if (wave_rows) {                                  // uniform per wave
           const float mref = prep(cur, p + u);
@@ -387,6 +451,7 @@ void pa_prefill_kernel(PrefillArgs a) {
         half(p, 0, sc_a, sc_b);
         half(p, 1, sc_b, sc_a);
       }
+
     }
 
     // rows at a negative position (more queries than cached tokens) are zero;
@@ -406,7 +471,42 @@ void pa_prefill_kernel(PrefillArgs a) {
           *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
         }
     }
+
     __syncthreads();                                    // LDS staging is reused by the next item
+  }
+}
+
+// Fused append, first part: the new tokens that share a block with cached
+// tokens (from the sequence's first new position up to the next block
+// boundary) are written to the pools here, before the prefill kernel reads
+// that block from the pools.  One workgroup per sequence; a sequence whose
+// new tokens start on a block boundary (a prompt, a block-aligned chunk)
+// has nothing to do.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_boundary_append_kernel(PrefillArgs a) {
+  constexpr int G = D / 8;                                // 16-byte units per head row
+  const int b = blockIdx.x;
+  const int n = rows_of(a, b);
+  const int ctx = clampi(a.context_lens[b], 0, a.ctx_limit);
+  const int bnd = ctx - n;                                // first new position
+  if (n == 0 || bnd <= 0 || bnd % kBlockTokens == 0) return;
+  const int cnt = min(kBlockTokens - bnd % kBlockTokens, n);
+  const int id = clampi(a.block_tables[(size_t)b * a.max_blocks + bnd / kBlockTokens], 0,
+                        a.num_blocks - 1);
+  const int units = cnt * a.H * G;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int g = u % G;
+    const int hh = (u / G) % a.H;
+    const int i = u / (G * a.H);
+    const int row = a.query_start[b] + i;
+    if (row < 0 || row >= a.num_rows) continue;
+    const int t = (bnd + i) % kBlockTokens;
+    const size_t src = ((size_t)row * a.H + hh) * D + 8 * g;
+    const size_t dst = ((((size_t)id * a.H + hh) * G + g) * kBlockTokens + t) * 8;
+    *reinterpret_cast<u4v*>(static_cast<_Float16*>(const_cast<void*>(a.k_pool)) + dst) =
+        *reinterpret_cast<const u4v*>(a.k_new + src);
+    *reinterpret_cast<u4v*>(static_cast<_Float16*>(const_cast<void*>(a.v_pool)) + dst) =
+        *reinterpret_cast<const u4v*>(a.v_new + src);
   }
 }
 
@@ -421,9 +521,26 @@ hipError_t launch_pa_prefill(const PrefillArgs& a, int D, int grid, int max_bloc
   const size_t lds = prefill_lds_bytes(a.B, max_blocks_used);
   const int threads = kWave * kPrefillWaves;
   if (D == 128)
-    hipLaunchKernelGGL((pa_prefill_kernel<128>), dim3(grid), dim3(threads), lds, stream, a);
+    hipLaunchKernelGGL((pa_prefill_kernel<128, false>), dim3(grid), dim3(threads), lds, stream, a);
   else
-    hipLaunchKernelGGL((pa_prefill_kernel<64>), dim3(grid), dim3(threads), lds, stream, a);
+    hipLaunchKernelGGL((pa_prefill_kernel<64, false>), dim3(grid), dim3(threads), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pa_prefill_append(const PrefillArgs& a, int D, int grid, int max_blocks_used,
+                                    hipStream_t stream) {
+  if (D == 128)
+    hipLaunchKernelGGL((prefill_boundary_append_kernel<128>), dim3(a.B), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_boundary_append_kernel<64>), dim3(a.B), dim3(256), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = prefill_lds_bytes(a.B, max_blocks_used);
+  const int threads = kWave * kPrefillWaves;
+  if (D == 128)
+    hipLaunchKernelGGL((pa_prefill_kernel<128, true>), dim3(grid), dim3(threads), lds, stream, a);
+  else
+    hipLaunchKernelGGL((pa_prefill_kernel<64, true>), dim3(grid), dim3(threads), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -220,10 +220,33 @@ def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale
     cache: row i of sequence b sits at position context_lens[b] - n_b + i.
     ``query_start`` is an int32 device tensor of B+1 entries; the other
     arguments are as for ``pa_decode``."""
+    return _prefill(q, None, None, k_pool, v_pool, block_tables, context_lens, query_start,
+                    scale, out, max_context_len)
+
+
+def pa_prefill_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_start,
+                      scale, out=None, *, max_context_len=None):
+    """``pa_prefill`` with the append of the new tokens fused in: row r of
+    k_new / v_new ([T][H][D] fp16, like q) is written to the slot of its
+    position (through the block table) in both pools, and the queries attend
+    as for ``pa_prefill``; ``context_lens`` counts the new tokens.  Pools and
+    output equal ``kv_append`` followed by ``pa_prefill`` bit for bit."""
+    return _prefill(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_start,
+                    scale, out, max_context_len)
+
+
+def _prefill(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+             out, max_context_len):
     lib = _lib.load_library()
     _need(q, "q", torch.float16, ndim=3)
     dev = q.device
     T, H, D = q.shape
+    append = k_new is not None
+    if append:
+        _need(k_new, "k_new", torch.float16, dev, ndim=3)
+        _need(v_new, "v_new", torch.float16, dev, ndim=3)
+        if tuple(k_new.shape) != (T, H, D) or tuple(v_new.shape) != (T, H, D):
+            raise ValueError("k_new and v_new must have the shape of q")
     NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
     if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
         raise ValueError("k_pool and v_pool differ in size")
@@ -240,12 +263,18 @@ def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale
     _need(out, "out", torch.float16, dev, ndim=3)
     if tuple(out.shape) != (T, H, D):
         raise ValueError("out must have the shape of q")
+    tail = (_ptr(block_tables), block_tables.shape[1], _ptr(context_lens), max_context_len,
+            _ptr(query_start), T, B, H, D, BLOCK_TOKENS, NB, float(scale), _ptr(out), 0,
+            _stream_handle(dev))
     with torch.cuda.device(dev):
-        code = lib.pkv_pa_prefill(
-            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
-            _ptr(context_lens), max_context_len, _ptr(query_start), T, B, H, D, BLOCK_TOKENS, NB,
-            float(scale), _ptr(out), 0, _stream_handle(dev))
-    _lib.check("pkv_pa_prefill", code)
+        if append:
+            name = "pkv_pa_prefill_append"
+            code = lib.pkv_pa_prefill_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                             _ptr(v_pool), *tail)
+        else:
+            name = "pkv_pa_prefill"
+            code = lib.pkv_pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), *tail)
+    _lib.check(name, code)
     return out
 
 

@@ -306,6 +306,30 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(qs=A16 + 2) == _lib.ERR_MISALIGNED
 
 
+def test_prefill_append_rejects_bad_arguments(lib):
+    f = lib.pkv_pa_prefill_append
+
+    def call(**kw):
+        a = dict(q=A16, kn=A16, vn=A16, k=A16, v=A16, tables=A16, mb=128, lens=A16, max_ctx=2048,
+                 qs=A16, T=512, B=8, H=32, D=128, bs=16, NB=64, scale=0.1, out=A16, flags=0)
+        a.update(kw)
+        return f(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["tables"], a["mb"], a["lens"],
+                 a["max_ctx"], a["qs"], a["T"], a["B"], a["H"], a["D"], a["bs"], a["NB"],
+                 a["scale"], a["out"], a["flags"], None)
+
+    # the checks of pkv_pa_prefill, then the new rows'
+    assert call(bs=8) == _lib.ERR_UNSUPPORTED
+    assert call(flags=1) == _lib.ERR_BAD_SHAPE
+    assert call(D=80) == _lib.ERR_BAD_SHAPE
+    assert call(mb=64) == _lib.ERR_BAD_SHAPE
+    assert call(T=0, kn=None) == _lib.OK and call(B=0, vn=None) == _lib.OK
+    assert call(kn=None) == _lib.ERR_NULL_PTR
+    assert call(vn=None) == _lib.ERR_NULL_PTR
+    assert call(k=None) == _lib.ERR_NULL_PTR
+    assert call(kn=A4) == _lib.ERR_MISALIGNED
+    assert call(vn=A16 + 8) == _lib.ERR_MISALIGNED
+
+
 def test_contig_decode_rejects_bad_arguments(lib):
     f = lib.pkv_contig_decode
 

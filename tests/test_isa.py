@@ -163,12 +163,15 @@ def prefill_asm(tmp_path_factory):
     return device_asm("pa_prefill.hip", tmp_path_factory.mktemp("isa"))
 
 
+@pytest.mark.parametrize("append", [False, True])
 @pytest.mark.parametrize("D", [128, 64])
-def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D):
+def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D, append):
     """The prefill's tile ring: 32x32x16 MFMAs, the K/V buffer resources stay
     scalar (no waterfall loop around a load), and three tiles stay in flight
-    (D/64 16-byte loads per thread and tile) at every wait."""
-    name = f"pa_prefill_kernelILi{D}E"
+    (D/64 16-byte loads per thread and tile) at every wait.  With the append
+    fused in, the per-tile choice of source (rows or pools) and the pool
+    writes keep that shape."""
+    name = f"pa_prefill_kernelILi{D}ELb{int(append)}E"
     body = kernel_body(prefill_asm, name)
     # the ring is the loop with the most MFMAs (the item loop around it
     # holds the first pair's score products and waits for each item's start)
