@@ -13,7 +13,7 @@ import torch
 import workloads as wl
 from oracle import append_ref, cow_ref, grouped_decode_ref, paged_decode_ref, paged_prefill_ref
 from paged_kv_cache_03_amd import (cow_copy_blocks, kv_append, pa_decode, pa_decode_append,
-                                   pa_decode_grouped, pa_prefill)
+                                   pa_decode_grouped, pa_prefill, pa_prefill_append)
 from tests._gpu import assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -163,6 +163,43 @@ def test_random_prefill(seed):
                      to_dev(qs), c.scale, max_context_len=int(max(lens.max(), 1)))
     torch.cuda.synchronize()
     assert_close(out, paged_prefill_ref(q, c.k_pool, c.v_pool, tables, lens, qs, c.scale), what)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_prefill_append(seed):
+    """The prefill with its append fused in: new tokens that start at 0, on
+    a block boundary or inside a block, more rows than positions; pools bit
+    exact against the oracle's append, outputs against the oracle."""
+    rng = np.random.default_rng(4500 + seed)
+    B = int(rng.integers(1, 13))
+    H = int(rng.choice([1, 2, 4, 6]))
+    D = int(rng.choice([64, 128]))
+    lens = _lens(rng, B, int(rng.choice([40, 300, 700])))
+    nq = np.array([min(int(n), int(rng.choice([16, 32, int(rng.integers(0, 200))])))
+                   if rng.random() < 0.8 else int(n) + int(rng.integers(0, 5)) for n in lens],
+                  dtype=np.int32)
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    tables, NB = _tables(rng, lens, int(rng.integers(0, 2)))
+    c = _case(rng, B, H, D, lens, tables, NB)
+    T = int(qs[-1])
+    q, kn, vn = (wl.normal_fp16(rng, (max(T, 1), H, D))[:T] for _ in range(3))
+    what = f"seed={seed} B={B} H={H} D={D} rows={T}"
+    print(what, flush=True)
+    if T == 0:
+        return
+    # slot of each new row: position lens[b] - n_b + i through the table, if not negative
+    slots = np.array([int(tables[b][p // 16]) * 16 + p % 16 if p >= 0 else -1
+                      for b in range(B) for p in range(int(lens[b]) - int(nq[b]), int(lens[b]))],
+                     dtype=np.int32)
+    kp, vp = to_dev(c.k_pool), to_dev(c.v_pool)
+    out = pa_prefill_append(to_dev(q), to_dev(kn), to_dev(vn), kp, vp, to_dev(tables),
+                            to_dev(lens), to_dev(qs), c.scale,
+                            max_context_len=int(max(lens.max(), 1)))
+    torch.cuda.synchronize()
+    k_ref, v_ref = append_ref(kn, vn, slots, c.k_pool, c.v_pool)
+    assert np.array_equal(to_host(kp).view(np.uint16), k_ref.view(np.uint16)), what
+    assert np.array_equal(to_host(vp).view(np.uint16), v_ref.view(np.uint16)), what
+    assert_close(out, paged_prefill_ref(q, k_ref, v_ref, tables, lens, qs, c.scale), what)
 
 
 @pytest.mark.parametrize("seed", range(6))
