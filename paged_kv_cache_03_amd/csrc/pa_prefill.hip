@@ -225,14 +225,15 @@ void pa_prefill_kernel(PrefillArgs a) {
     const bool loader = wave * kWave < kLoaders;        // uniform per wave
     auto unit_is_v = [&](int k) { return wave * kWave + kLoaders * k >= kTileUnits; };
     const uint32_t unit_off = (uint32_t)(tid % kTileUnits) * 16u;
-    // Rows source (fused append): in a tile read from the caller's rows this
-    // thread's unit is token t_r, dims 8 g_r .. +7 (16 consecutive lanes read
-    // one token's row of the head, 2 D bytes), which is unit u_r of the
-    // pool's tile layout.  row_r is the row of token t_r of block 0.
-    const int ur = tid % kTileUnits;
-    const int t_r = ur / (D / 8);
-    const int g_r = ur % (D / 8);
-    const int u_r = g_r * kBlockTokens + t_r;
+    // Rows source (fused append): a thread holds the same unit of a tile
+    // read from the caller's rows as of a pool tile, u_r = 16 g_r + t_r
+    // (token t_r, dims 8 g_r .. +7), so both stage into the same LDS slot
+    // without bank conflicts; in the rows, 4 lanes of a wave read 64
+    // consecutive bytes of each of 16 token rows.  row_r is the row of
+    // token t_r of block 0.
+    const int u_r = tid % kTileUnits;
+    const int t_r = u_r % kBlockTokens;
+    const int g_r = u_r / kBlockTokens;
     const int row_r = a.query_start[b] - bnd + t_r;
     const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
     const uint32_t rows_total = (uint32_t)a.num_rows * row_bytes;
@@ -276,9 +277,8 @@ void pa_prefill_kernel(PrefillArgs a) {
           }
         }
       };
-      // Stage block j's tiles (pool offset o) into pair slot half st (a tile
-      // read from the rows holds unit u_r where a pool tile holds unit u).
-      // With the append, a tile read from the rows also goes to its pool
+      // Stage block j's tiles (pool offset o) into pair slot half st.  With
+      // the append, a tile read from the rows also goes to its pool
       // block when this item owns the block (its rows hold the block's first
       // token): the store is issued for every tile, with an empty range when
       // the item does not own it, so the ring's wait counts stay fixed.
@@ -286,10 +286,9 @@ void pa_prefill_kernel(PrefillArgs a) {
         if (!loader) return;                              // uniform per wave
         const int u = tid % kTileUnits;
         const bool rows = kAppend && j >= jn;             // uniform
-        const int slot = rows ? u_r : u;
   #pragma unroll
         for (int k = 0; k < kUnits; ++k)
-          s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(slot) : slot] = r[k];
+          s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(u) : u] = r[k];
         if constexpr (kAppend) {
           const bool own = rows && j < nblk && (kBlockTokens * j - bnd) / kPrefillRows == kq;
           const uint32_t woff = t_r < ctx - kBlockTokens * j ? (uint32_t)u_r * 16u : 0xFFFFFFF0u;
