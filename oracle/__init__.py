@@ -30,7 +30,6 @@ from .paged_attention import (  # noqa: F401
     gather_ref,
     pool_element_index,
     paged_decode_ref,
-    paged_decode_rows_ref,
 )
 from .cache_ops import append_ref, cow_ref  # noqa: F401
 from .grouped import grouped_decode_ref, grouped_tables_ref  # noqa: F401

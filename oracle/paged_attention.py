@@ -31,8 +31,6 @@ Readings where the pages are silent:
   token 15.  ``pool_element_index`` spells this out element by element.
 """
 
-import math
-
 import numpy as np
 
 # Tokens per page ("Atención paginada ...", 7minutos.es, PagePool part:
@@ -142,23 +140,3 @@ def paged_decode_ref(q, k_pool, v_pool, block_tables, context_lens, scale, seqs=
         V = gather_ref(v_pool, block_tables[b], n, H, D)
         out[b] = attention_ref(q[b], K, V, scale)
     return out
-
-
-def paged_decode_rows_ref(q_rows, k_pool, v_pool, tables, lens, scale):
-    """``paged_decode_ref`` over a list of (q[H][D], table, n) rows, returning
-    a float64 [rows][H][D] array; used for sampled checks at full size."""
-    q_rows = np.asarray(q_rows)
-    R, H, D = q_rows.shape
-    out = np.empty((R, H, D), dtype=np.float64)
-    for r in range(R):
-        n = int(lens[r])
-        K = gather_ref(k_pool, tables[r], n, H, D)
-        V = gather_ref(v_pool, tables[r], n, H, D)
-        out[r] = attention_ref(q_rows[r], K, V, scale)
-    return out
-
-
-def scaled_dim(head_dim):
-    """1/sqrt(d) as the float32 value the workloads pass ("Formulació
-    matemàtica": d is the attention dimension)."""
-    return float(np.float32(1.0 / math.sqrt(head_dim)))
