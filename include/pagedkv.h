@@ -16,7 +16,10 @@
  * context_lens entry above max_context_len) are not reported: the kernels
  * clamp or skip them so that no access leaves the buffers (a context is
  * clamped to max_context_len), and the results for the affected rows are
- * unspecified.
+ * unspecified.  A block id outside the pool is clamped for reading only:
+ * every call that writes the pools (the appends, fused or not, and the
+ * copy-on-write) writes nothing for it, so no other sequence's block is
+ * touched.
  *
  * Sources: "PagedAttention" (e-fortepiano.pl, Catalan encyclopedia
  * article), sections "Descripció" and "Formulació matemàtica"; "Atención
@@ -320,7 +323,11 @@ int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
  * from the pools; the new tokens of a block that also holds cached tokens
  * are written by a first, small kernel, so any split of a sequence into
  * chunks is allowed.  Pools and out equal those of the two separate calls
- * bit for bit.
+ * bit for bit, provided no block that receives new tokens of one sequence
+ * appears in another sequence's table in the same call: the other sequence
+ * would read that block from the pools while it is being written (a
+ * prompt prefix shared by several sequences is written by one call and
+ * shared afterwards, or copied first, see pkv_cow_copy_blocks).
  *
  * device: k_new, v_new [num_query_rows][H][D] fp16 (16-byte aligned), the
  *         rest as for pkv_pa_prefill; k_pool and v_pool are written.

@@ -18,3 +18,4 @@ from .ops import (VirtualKV, contig_decode, contig_decode_rows,  # noqa: F401
                   kv_append, pa_decode, pa_decode_append,
                   pa_decode_grouped, pa_decode_grouped_workspace_size, pa_decode_workspace_size,
                   pa_prefill, pa_prefill_append, pool_shape)
+from .validate import ContractError, debug_enabled, set_debug  # noqa: F401

@@ -372,8 +372,9 @@ __global__ __launch_bounds__(256) void pa_decode_flat_merge_kernel(FlatArgs a) {
     const bool is_v = lane >= D / 8;
     const u4v row_new =
         reinterpret_cast<const u4v*>((is_v ? a.v_new : a.k_new) + (size_t)bh * D)[g];
-    if (ctx > 0 && lane < 2 * (D / 8)) {
-      const size_t blk = (size_t)min(max(id, 0), a.num_blocks - 1);
+    // a table entry outside the pool writes nothing, as in kv_append
+    if (ctx > 0 && lane < 2 * (D / 8) && (unsigned)id < (unsigned)a.num_blocks) {
+      const size_t blk = (size_t)id;
       u4v* dst = reinterpret_cast<u4v*>(const_cast<void*>(is_v ? a.v_pool : a.k_pool));
       dst[((blk * a.H + h) * (D / 8) + g) * kBlockTokens + t % kBlockTokens] = row_new;
     }

@@ -173,9 +173,12 @@ void pa_prefill_kernel(PrefillArgs a) {
     const int bnd = ctx - n;
     const int jn = kAppend ? (max(bnd, 0) + kBlockTokens - 1) / kBlockTokens : 0x7fffffff;
 
+    // Block ids, clamped into the pool for reading.  With the append, an
+    // entry outside the pool also sets bit 31, so the block is never written.
     for (int j = tid; j < nblk; j += blockDim.x) {
       const int id = a.block_tables[(size_t)b * a.max_blocks + j];
-      s_ids[j] = clampi(id, 0, a.num_blocks - 1);
+      const int in_pool = clampi(id, 0, a.num_blocks - 1);
+      s_ids[j] = kAppend && in_pool != id ? (int)((uint32_t)in_pool | 0x80000000u) : in_pool;
     }
     __syncthreads();
 
@@ -257,10 +260,14 @@ void pa_prefill_kernel(PrefillArgs a) {
       const int v_last = ctx - (nblk - 1) * kBlockTokens;   // valid tokens of the last block
       const uint32_t v_off_last =
           (int)((tid % kTileUnits) % kBlockTokens) < v_last ? unit_off : 0x7FFFFFF0u;
+      // o returns the block's pool offset; with the append its bit 0 is set
+      // when the table entry lies outside the pool (offsets are multiples of
+      // a tile, so bit 0 is free).
       auto fetch = [&](u4v (&r)[kUnits], size_t& o, int j) {
         const int jj = min(j, nblk - 1);
         const uint32_t bytes = j < nblk && loader ? kTile : 0u;
-        o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
+        const int raw = __builtin_amdgcn_readfirstlane(s_ids[jj]);
+        o = (size_t)(raw & 0x7fffffff) * block_stride;
         const bool rows = kAppend && j >= jn;             // uniform
         const uint32_t roff = kAppend ? row_off(j) : 0u;
   #pragma unroll
@@ -276,6 +283,7 @@ void pa_prefill_kernel(PrefillArgs a) {
             r[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(pool, bytes), off, 0, 0);
           }
         }
+        if constexpr (kAppend) o |= (size_t)(raw < 0);
       };
       // Stage block j's tiles (pool offset o) into pair slot half st.  With
       // the append, a tile read from the rows also goes to its pool
@@ -290,12 +298,15 @@ void pa_prefill_kernel(PrefillArgs a) {
         for (int k = 0; k < kUnits; ++k)
           s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(u) : u] = r[k];
         if constexpr (kAppend) {
-          const bool own = rows && j < nblk && (kBlockTokens * j - bnd) / kPrefillRows == kq;
+          // a block whose table entry lies outside the pool is not written
+          const bool own = rows && j < nblk && !(o & 1) &&
+                           (kBlockTokens * j - bnd) / kPrefillRows == kq;
+          const size_t ob = o & ~(size_t)1;
           const uint32_t woff = t_r < ctx - kBlockTokens * j ? (uint32_t)u_r * 16u : 0xFFFFFFF0u;
   #pragma unroll
           for (int k = 0; k < kUnits; ++k)
             __builtin_amdgcn_raw_buffer_store_b128(
-                r[k], make_rsrc(const_cast<char*>((unit_is_v(k) ? vbase : kbase) + o),
+                r[k], make_rsrc(const_cast<char*>((unit_is_v(k) ? vbase : kbase) + ob),
                                 own ? kTile : 0u),
                 woff, 0, 0);
         }
@@ -490,8 +501,8 @@ __global__ __launch_bounds__(256) void prefill_boundary_append_kernel(PrefillArg
   const int bnd = ctx - n;                                // first new position
   if (n == 0 || bnd <= 0 || bnd % kBlockTokens == 0) return;
   const int cnt = min(kBlockTokens - bnd % kBlockTokens, n);
-  const int id = clampi(a.block_tables[(size_t)b * a.max_blocks + bnd / kBlockTokens], 0,
-                        a.num_blocks - 1);
+  const int id = a.block_tables[(size_t)b * a.max_blocks + bnd / kBlockTokens];
+  if ((unsigned)id >= (unsigned)a.num_blocks) return;   // outside the pool: nothing written
   const int units = cnt * a.H * G;
   for (int u = threadIdx.x; u < units; u += blockDim.x) {
     const int g = u % G;

@@ -12,7 +12,7 @@ import ctypes
 
 import torch
 
-from . import _lib
+from . import _lib, validate
 
 BLOCK_TOKENS = 16
 
@@ -148,6 +148,8 @@ def pa_decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, dev)
         ws_bytes = workspace.numel()
+    if validate.debug_enabled():
+        validate.check_decode_append(block_tables, context_lens)
     with torch.cuda.device(dev):
         code = lib.pkv_pa_decode_append(
             _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
@@ -263,6 +265,8 @@ def _prefill(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_
     _need(out, "out", torch.float16, dev, ndim=3)
     if tuple(out.shape) != (T, H, D):
         raise ValueError("out must have the shape of q")
+    if append and validate.debug_enabled():
+        validate.check_prefill_append(block_tables, context_lens, query_start)
     tail = (_ptr(block_tables), block_tables.shape[1], _ptr(context_lens), max_context_len,
             _ptr(query_start), T, B, H, D, BLOCK_TOKENS, NB, float(scale), _ptr(out), 0,
             _stream_handle(dev))
@@ -430,6 +434,8 @@ def kv_append(k, v, slot_mapping, k_pool, v_pool):
     NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
     if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
         raise ValueError("k_pool and v_pool differ in size")
+    if validate.debug_enabled():
+        validate.check_slots(slot_mapping, NB)
     with torch.cuda.device(dev):
         code = lib.pkv_kv_append(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_pool),
                                  _ptr(v_pool), NB, H, D, BLOCK_TOKENS, _stream_handle(dev))
@@ -456,6 +462,8 @@ def cow_copy_blocks(src_dst_pairs, k_pools, v_pools):
             raise ValueError("all pools must have the same shape")
     NB = first.shape[0]
     block_bytes = first[0].numel() * first.element_size()
+    if validate.debug_enabled():
+        validate.check_cow_pairs(src_dst_pairs, NB)
     L = len(k_pools)
     karr = (ctypes.c_void_p * L)(*[p.data_ptr() for p in k_pools])
     varr = (ctypes.c_void_p * L)(*[p.data_ptr() for p in v_pools])

@@ -51,3 +51,28 @@ def test_traffic_record_calibrates_and_sums(tmp_path, monkeypatch):
     json.dump(rec, open(tmp_path / "traffic.json", "w"))
     assert bench.measured_traffic() is None
 
+
+
+def test_full_step_bytes_match_the_pages_per_token_figure():
+    """The full decode step (32 layers x 200 sequences x 2048 tokens, 32
+    heads x 128, fp16) moves K and V of 200 x 2048 tokens through every
+    layer: the bench's per-layer K/V bytes summed over the 32 layers equal
+    200 x 2048 x 524,288 B = 214,748,364,800 B, where 524,288 B (512 KiB)
+    is the per-token cache size of "Atención paginada en modelos de lenguaje
+    grandes (LLM)" (7minutos.es, bytes-per-token part: 2 (K and V) x 32
+    layers x 32 heads x 128 dims x 2 bytes)."""
+    import json
+    import os
+
+    import workloads as wl
+    from paged_kv_cache_03_amd import kv_bytes_per_token
+
+    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                         "pages_worked_examples.json")))
+    per_token = golden["bytes_per_token"]["bytes"]
+    c = wl.full_step()
+    assert c.num_layers == 32 and len(c.context_lens) == 200
+    total = sum(bench.algorithmic_bytes(c.context_lens, c.num_heads, c.head_dim)[0]
+                for _ in range(c.num_layers))
+    assert kv_bytes_per_token(32, 32, 128) == per_token == 524288
+    assert total == 200 * 2048 * kv_bytes_per_token(32, 32, 128) == 214_748_364_800

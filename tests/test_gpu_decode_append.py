@@ -151,3 +151,34 @@ def test_repeated_steps_grow_the_cache():
         torch.cuda.synchronize()
         assert torch.equal(out_a, out_b), f"step {s}"
     assert torch.equal(_bits(kp_a), _bits(kp_b)) and torch.equal(_bits(vp_a), _bits(vp_b))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_new_token_block_outside_the_pool_is_not_written(D):
+    """A sequence whose last table entry is -1 (the caller did not allocate
+    the block) and one whose entry is past the pool: the fused call writes
+    neither token anywhere, exactly as kv_append skips those slots, so the
+    pools equal kv_append's bit for bit (and the oracle's append of the
+    other rows); every other sequence's output equals the separate calls'
+    and the oracle's.  Reads of such entries are clamped into the pool, so
+    the test stays in bounds."""
+    H = 4
+    lens = [17, 33, 1, 40, 16, 100, 64, 5]
+    q, k_new, v_new, kp, vp, tables, lens = _ragged(81 + D, H, D, lens)
+    NB = kp.shape[0]
+    bad = {0: -1, 2: NB + 7, 4: -1, 6: NB}     # sequence -> its last block's table entry
+    for b, ent in bad.items():
+        tables[b, (int(lens[b]) - 1) // 16] = ent
+    scale = float(np.float32(D ** -0.5))
+    (kp1, vp1, out1), (kp2, vp2, out2), slots = _both_ways(
+        q, k_new, v_new, to_dev(kp), to_dev(vp), tables, lens, scale, int(lens.max()))
+    assert torch.equal(_bits(kp1), _bits(kp2)) and torch.equal(_bits(vp1), _bits(vp2))
+    inside = (slots >= 0) & (slots < NB * 16)
+    assert inside.sum() == len(lens) - len(bad)
+    k_ref, v_ref = append_ref(k_new[inside], v_new[inside], slots[inside], kp, vp)
+    assert np.array_equal(to_host(kp2).view(np.uint16), k_ref.view(np.uint16))
+    assert np.array_equal(to_host(vp2).view(np.uint16), v_ref.view(np.uint16))
+    good = [b for b in range(len(lens)) if b not in bad]
+    assert torch.equal(out1[good], out2[good])
+    ref = paged_decode_ref(q, k_ref, v_ref, tables, lens, scale, seqs=good)
+    assert_close(out2, ref, f"fused append, entries outside the pool, D={D}")

@@ -84,3 +84,31 @@ def test_other_streams_alone_and_concurrent():
             assert torch.equal(outs[i], ref[i]), f"stream {i}, repetition {rep}"
     assert_close(ref[0], paged_decode_ref(ca.q, ca.k_pool, ca.v_pool, ca.block_tables,
                                           ca.context_lens, ca.scale), "batch 64 default stream")
+
+
+def test_debug_mode_rejects_contract_violations_before_launch():
+    """With the host checks on, conflicting copy pairs, a slot written twice
+    and a fused append into a block another sequence reads raise
+    ContractError before anything is enqueued: the pools stay as they were.
+    With the checks off the same calls are not inspected."""
+    from paged_kv_cache_03_amd import ContractError, cow_copy_blocks, kv_append, set_debug
+
+    H, D, NB = 2, 64, 8
+    kp = torch.randn(wl.pool_shape(NB, H, D), device=dev()).half()
+    vp = torch.randn(wl.pool_shape(NB, H, D), device=dev()).half()
+    k0, v0 = kp.clone(), vp.clone()
+    rows = torch.randn(3, H, D, device=dev()).half()
+    old = set_debug(True)
+    try:
+        with pytest.raises(ContractError):
+            cow_copy_blocks(to_dev(np.array([[1, 5], [2, 5]], dtype=np.int32)), [kp], [vp])
+        with pytest.raises(ContractError):
+            kv_append(rows, rows, to_dev(np.array([3, 4, 3], dtype=np.int32)), kp, vp)
+        tables = to_dev(np.array([[4, 5], [4, 6]], dtype=np.int32))
+        with pytest.raises(ContractError):
+            pa_decode_append(rows[:2].contiguous(), rows[:2].contiguous(), rows[:2].contiguous(),
+                             kp, vp, tables, to_dev(np.array([16, 30], dtype=np.int32)), 0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(kp, k0) and torch.equal(vp, v0)
+    finally:
+        set_debug(old)

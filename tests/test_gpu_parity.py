@@ -314,3 +314,37 @@ def test_block_manager_end_to_end():
             checked += 1
     assert checked >= 15
     pool.check()
+
+
+def test_plain_entry_point_at_the_headline_shape():
+    """``pkv_pa_decode`` itself, called through ctypes with its own
+    signature (no binding in between) on the batch-200 workload (32 heads x
+    128, contexts up to 2048): its output equals ``pkv_pa_decode_ex`` with
+    the default partition and no flags bit for bit, and all 200 sequences
+    match the float64 oracle within max-abs 2e-3 and relative L2 1e-3."""
+    import ctypes
+
+    lib = _lib.load_library()
+    c = wl.gpt_batch(200, seed=2, append=True)   # the headline batch; decoded as it stands
+    kp, vp = device_pools(c)
+    q, tables, lens = to_dev(c.q), to_dev(c.block_tables), to_dev(c.context_lens)
+    B, H, D = c.q.shape
+    NB = kp.shape[0]
+    ws_bytes = lib.pkv_pa_decode_workspace_size(B, H, D, c.max_context)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    i32p = lambda t: ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    outs = []
+    for ex in (False, True):
+        out = torch.full((B, H, D), float("nan"), dtype=torch.float16, device=dev())
+        common = (p(q), p(kp), p(vp), i32p(tables), tables.shape[1], i32p(lens), c.max_context,
+                  B, H, D, 16, NB, ctypes.c_float(c.scale), p(out), p(ws), ws_bytes)
+        print(f"pkv_pa_decode{'_ex' if ex else ''}: B={B} H={H} D={D} NB={NB}", flush=True)
+        code = lib.pkv_pa_decode_ex(*common, 0, 0, stream) if ex else \
+            lib.pkv_pa_decode(*common, stream)
+        assert code == 0, lib.pkv_status_string(code)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert_close(outs[0], oracle(c, c.k_pool, c.v_pool), "pkv_pa_decode, batch 200")

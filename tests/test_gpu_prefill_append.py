@@ -132,3 +132,43 @@ def test_chunked_workload(cached):
                           natural_slots(c.block_tables, c.context_lens, c.query_start))
     _check(c.q, c.k_new, c.v_new, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
            c.query_start, c.scale, f"chunked workload over {cached}, fused", seqs=[0, 13, 31])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_new_token_blocks_outside_the_pool_are_not_written(D):
+    """Table entries of blocks holding new tokens set to -1 or past the
+    pool: the block shared with cached tokens (written by the boundary
+    kernel) and all-new blocks (written while staged).  Nothing is written
+    for them, as kv_append skips those slots, so the pools equal kv_append's
+    and the oracle's append of the remaining rows bit for bit; the other
+    sequences' outputs equal the separate calls' and the oracle's.  Reads of
+    such entries are clamped into the pool, so the test stays in bounds."""
+    H = 4
+    lens = [70, 150, 48, 200, 37, 400]
+    nq = [20, 100, 16, 200, 37, 250]
+    q, k_new, v_new, kp, vp, tables, lens, qs = _case(83 + D, H, D, lens, nq)
+    NB = kp.shape[0]
+    # sequence 0: new tokens start at 50, inside block 3 (boundary kernel)
+    # sequence 1: new tokens 50..149; block 5 is all new, past the pool
+    # sequence 3: a prompt; blocks 0 and 7 all new, -1 and past the pool
+    # sequence 5: new tokens 150..399; block 9 (boundary, -1), block 20 (-1)
+    bad = {(0, 3): -1, (1, 5): NB + 3, (3, 0): -1, (3, 7): NB, (5, 9): -1, (5, 20): -1}
+    for (b, j), ent in bad.items():
+        tables[b, j] = ent
+    affected = sorted({b for b, _ in bad})
+    scale = float(np.float32(D ** -0.5))
+    out_f, kf, vf, out_s, ks, vs, slots = _both(q, k_new, v_new, kp, vp, tables, lens, qs,
+                                                scale, int(lens.max()))
+    assert torch.equal(kf.view(torch.int16), ks.view(torch.int16))
+    assert torch.equal(vf.view(torch.int16), vs.view(torch.int16))
+    inside = (slots >= 0) & (slots < NB * 16)
+    # new positions that fall in the bad blocks: 14 + 16 + 16 + 16 + 10 + 16
+    assert (~inside).sum() == 88
+    k_ref, v_ref = append_ref(k_new[inside], v_new[inside], slots[inside], kp, vp)
+    assert np.array_equal(to_host(kf).view(np.uint16), k_ref.view(np.uint16))
+    assert np.array_equal(to_host(vf).view(np.uint16), v_ref.view(np.uint16))
+    good = [b for b in range(len(lens)) if b not in affected]
+    rows = np.concatenate([np.arange(qs[b], qs[b + 1]) for b in good])
+    assert torch.equal(out_f[rows], out_s[rows])
+    ref = paged_prefill_ref(q, k_ref, v_ref, tables, lens, qs, scale, seqs=good)
+    assert_close(out_f, ref, f"fused prefill, entries outside the pool, D={D}")
