@@ -64,7 +64,9 @@ enum pkv_status {
                                       (int32 arrays: 4-byte) */
   PKV_ERR_UNSUPPORTED = 4,         /* block_size other than 16 */
   PKV_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the required size */
-  PKV_ERR_HIP = 6                  /* the HIP runtime reported a launch error */
+  PKV_ERR_HIP = 6,                 /* the HIP runtime reported a launch error */
+  PKV_ERR_SCRATCH_TOO_SMALL = 7    /* the shape needs more than the library's fixed
+                                      scratch buffer (PKV_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* Tokens per physical block ("Atención paginada ...", 7minutos.es,
@@ -172,6 +174,38 @@ int pkv_pa_decode_append(const void* q, const void* k_new, const void* v_new,
                          int32_t block_size, int32_t num_blocks, float scale,
                          void* out, void* workspace, size_t workspace_bytes,
                          uint32_t flags, void* stream);
+
+/*
+ * pkv_pa_decode_append for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels, pools and
+ * output as pkv_pa_decode_append (bit for bit), minus the workspace: the
+ * partial results live in a fixed device array of the library,
+ * PKV_NOALLOC_SCRATCH_BYTES bytes on every GPU it runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocation); its first call on a device looks up that device's copy of
+ * the array, with the device current.
+ *
+ * Limit: shapes whose pkv_pa_decode_workspace_size exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES return PKV_ERR_SCRATCH_TOO_SMALL before any HIP
+ * call (4 MiB holds every shape the fused call accepts up to H = 2048: the
+ * flat plan needs about 2 MiB of partials at D = 128 plus 4 (B + 1) bytes).
+ * The array's contents are left from the previous call and need no
+ * clearing (every partial is written before it is read).  All calls on one
+ * GPU share the one array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give unspecified results; calls ordered on one stream are safe.
+ *
+ * Errors as for pkv_pa_decode_append, plus PKV_ERR_SCRATCH_TOO_SMALL, and
+ * PKV_ERR_HIP when the array's device address cannot be looked up.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int pkv_pa_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                 void* k_pool, void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int32_t B, int32_t H, int32_t D,
+                                 int32_t block_size, int32_t num_blocks, float scale,
+                                 void* out, uint32_t flags, void* stream);
 
 size_t pkv_pa_decode_workspace_size_ex(int32_t B, int32_t H, int32_t D,
                                        int32_t max_context_len,

@@ -15,7 +15,7 @@ from .blocks import (PAGE_TOKENS, PagedRequest, PagePool, PoolExhausted,  # noqa
 from .ops import (VirtualKV, contig_decode, contig_decode_rows,  # noqa: F401
                   contig_decode_workspace_size,
                   cow_copy_blocks, default_partition,
-                  kv_append, pa_decode, pa_decode_append,
+                  kv_append, pa_decode, pa_decode_append, pa_decode_append_noalloc,
                   pa_decode_grouped, pa_decode_grouped_workspace_size, pa_decode_workspace_size,
                   pa_prefill, pa_prefill_append, pool_shape)
 from .validate import ContractError, debug_enabled, set_debug  # noqa: F401

@@ -21,6 +21,8 @@ ERR_MISALIGNED = 3
 ERR_UNSUPPORTED = 4
 ERR_WORKSPACE_TOO_SMALL = 5
 ERR_HIP = 6
+ERR_SCRATCH_TOO_SMALL = 7
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # Every symbol include/pagedkv.h declares, with its ctypes signature.
 _c = ctypes
@@ -59,6 +61,9 @@ SIGNATURES = {
     "pkv_pa_decode_append": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _i32p, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _c.c_float, _vp, _vp,
                                          _c.c_size_t, _c.c_uint32, _vp]),
+    "pkv_pa_decode_append_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _i32p,
+                                                 _i32, _i32, _i32, _i32, _i32, _i32, _c.c_float,
+                                                 _vp, _c.c_uint32, _vp]),
     "pkv_kv_append": (_c.c_int, [_vp, _vp, _i32p, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pkv_cow_copy_blocks": (_c.c_int, [_c.POINTER(_vp), _c.POINTER(_vp), _i32, _i32p, _i32, _i32,
                                        _c.c_int64, _vp]),

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "pagedkv.h"
 
@@ -143,6 +145,37 @@ bool group_shape_ok(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int32_t G,
 
 }  // namespace
 
+// Scratch of pkv_pa_decode_append_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` only names the symbol; kernels get
+// the device address that device_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on
+// the first call on that device (with it current) and kept.
+hipError_t device_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t pkv_abi_version(void) { return kAbiVersion; }
@@ -156,6 +189,8 @@ const char* pkv_status_string(int code) {
     case PKV_ERR_UNSUPPORTED: return "unsupported block size (only 16 tokens per block)";
     case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than pkv_pa_decode_workspace_size";
     case PKV_ERR_HIP: return "HIP runtime error at launch";
+    case PKV_ERR_SCRATCH_TOO_SMALL:
+      return "shape needs more than the fixed scratch buffer (PKV_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -185,7 +220,8 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool,
                 const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H,
                 int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
                 void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                uint32_t flags, const void* k_new, const void* v_new, void* stream) {
+                uint32_t flags, const void* k_new, const void* v_new, void* stream,
+                bool use_scratch = false) {
   const bool append = k_new != nullptr || v_new != nullptr;
   if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
   if (flags & ~(uint32_t)PKV_DECODE_KEEP_KV_CACHED) return PKV_ERR_BAD_SHAPE;
@@ -205,6 +241,11 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool,
 
   const Plan plan = make_plan(B, H, D, max_context_len, partition_tokens);
   if (append && !plan.flat) return PKV_ERR_UNSUPPORTED;
+  if (use_scratch) {                   // the library's array instead of a workspace
+    if (plan.total > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH_TOO_SMALL;
+    if (device_scratch(&workspace) != hipSuccess) return PKV_ERR_HIP;
+    workspace_bytes = PKV_NOALLOC_SCRATCH_BYTES;
+  }
   if (plan.total > 0) {
     if (!workspace) return PKV_ERR_NULL_PTR;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_MISALIGNED;
@@ -295,6 +336,18 @@ int pkv_pa_decode_append(const void* q, const void* k_new, const void* v_new, vo
   return decode_impl(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, B, H, D, block_size, num_blocks, scale, out, workspace,
                      workspace_bytes, 0, flags, k_new, v_new, stream);
+}
+
+int pkv_pa_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                 void* k_pool, void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int32_t B, int32_t H, int32_t D,
+                                 int32_t block_size, int32_t num_blocks, float scale, void* out,
+                                 uint32_t flags, void* stream) {
+  if (!k_new || !v_new) return PKV_ERR_NULL_PTR;
+  return decode_impl(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, B, H, D, block_size, num_blocks, scale, out, nullptr, 0, 0,
+                     flags, k_new, v_new, stream, true);
 }
 
 int pkv_pa_decode(const void* q, const void* k_pool, const void* v_pool,

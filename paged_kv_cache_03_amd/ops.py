@@ -215,6 +215,39 @@ def pa_decode_grouped(q, k_pool, v_pool, block_tables, context_lens, group_offse
     return out
 
 
+def pa_decode_append_noalloc(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                             out, *, max_context_len, keep_cached=False):
+    """``pa_decode_append`` through ``pkv_pa_decode_append_noalloc``: no
+    workspace, nothing allocated (the caller passes ``out`` and
+    ``max_context_len``); the partial results live in the library's fixed
+    per-GPU scratch array, so calls that overlap on one GPU race."""
+    lib = _lib.load_library()
+    _need(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    B, H, D = q.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("out", out)):
+        _need(t, name, torch.float16, dev, ndim=3)
+        if tuple(t.shape) != (B, H, D):
+            raise ValueError(f"{name} must be [B][H][D] like q")
+    NB = _pool_blocks(k_pool, "k_pool", H, D, dev)
+    if _pool_blocks(v_pool, "v_pool", H, D, dev) != NB:
+        raise ValueError("k_pool and v_pool differ in size")
+    _need(block_tables, "block_tables", torch.int32, dev, ndim=2)
+    _need(context_lens, "context_lens", torch.int32, dev, ndim=1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens do not match the batch")
+    if validate.debug_enabled():
+        validate.check_decode_append(block_tables, context_lens)
+    with torch.cuda.device(dev):
+        code = lib.pkv_pa_decode_append_noalloc(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, H, D,
+            BLOCK_TOKENS, NB, float(scale), _ptr(out),
+            _lib.DECODE_KEEP_KV_CACHED if keep_cached else 0, _stream_handle(dev))
+    _lib.check("pkv_pa_decode_append_noalloc", code)
+    return out
+
+
 def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, out=None, *,
                max_context_len=None):
     """Causal attention of each sequence's last n_b cached tokens (its rows

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
     assert lib.pkv_abi_version() == _lib.ABI_VERSION
@@ -371,3 +371,29 @@ def test_vkv_rejects_bad_arguments(lib):
     info = _lib.VkvInfo()
     assert lib.pkv_vkv_stats(None, ctypes.byref(info)) == _lib.ERR_NULL_PTR
     assert lib.pkv_vkv_append(None, 0, A16, A16, A16, A16, 4, None) == _lib.ERR_NULL_PTR
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """The allocation-free decode step checks its fixed scratch size before
+    any HIP call: 4,096 heads need 8,192 partial rows of 128 floats, more
+    than PKV_NOALLOC_SCRATCH_BYTES; other errors as for the workspace call."""
+    assert lib.pkv_pa_decode_workspace_size(1, 4096, 128, 16) > _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.pkv_pa_decode_workspace_size(200, 32, 128, 2048) <= _lib.NOALLOC_SCRATCH_BYTES
+
+    def call(**kw):
+        a = dict(q=A16, kn=A16, vn=A16, k=A16, v=A16, tables=A16, maxb=128, ctx=A16,
+                 maxctx=2048, B=4, H=32, D=128, bs=16, nb=1024, out=A16, flags=0)
+        a.update(kw)
+        return lib.pkv_pa_decode_append_noalloc(
+            a["q"], a["kn"], a["vn"], a["k"], a["v"], a["tables"], a["maxb"], a["ctx"],
+            a["maxctx"], a["B"], a["H"], a["D"], a["bs"], a["nb"], 0.088, a["out"], a["flags"],
+            None)
+
+    assert call(B=1, H=4096, maxctx=16, maxb=1) == _lib.ERR_SCRATCH_TOO_SMALL
+    assert call(kn=None) == _lib.ERR_NULL_PTR
+    assert call(out=None) == _lib.ERR_NULL_PTR
+    assert call(bs=32) == _lib.ERR_UNSUPPORTED
+    assert call(D=96) == _lib.ERR_BAD_SHAPE
+    assert call(q=MIS) == _lib.ERR_MISALIGNED
+    assert call(flags=4) == _lib.ERR_BAD_SHAPE
+    assert call(B=0) == _lib.OK
