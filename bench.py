@@ -8,6 +8,17 @@ one layer of a GPT-style model, batch 200, 32 heads x 128 dims, fp16,
 capped at 2048, pool = blocks needed + 10% free, tables from a shuffled free
 list (seed 2).  Inputs are resident in HBM before the timed region.
 
+The default run then times the other workloads in the same process (batch
+10, the shared prefix with the grouped decode, the 32-layer full step, the
+4-beam full step, the prompt prefill and the chunked prefill) and adds a
+summary of each (step time and rate, call time, roofline on its own bytes,
+seq-layers/s, its own CPU baseline) under ``other_workloads``; ``--workload``
+runs one of them alone, ``--no-extras`` skips them.
+
+The CPU baseline is the float64 oracle on a bounded sample of each workload,
+run by a child process that never touches the GPU, over a pool of up to 16
+worker processes with one BLAS thread each, next to a single-core figure.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: the library runs on
 one GPU (there is no multi-GPU path).
 """
@@ -30,7 +41,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -41,9 +52,10 @@ def parse():
                              "prefill_prompt", "prefill_chunked", "vattention"],
                     help="batch200 (default): the headline one-layer batch of 200")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=0,
-                    help="sequences (groups, for the grouped decode) in the oracle sample "
-                         "(0 = sized to about 15 s)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload only: skip timing the other workloads (batch 10, "
+                         "shared prefix, full step, 4-beam step, both prefills) in the same run")
+    ap.add_argument("--cpu-worker", metavar="DIR", help=argparse.SUPPRESS)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     ap.add_argument("--decode", choices=["auto", "flat", "grouped"], default="auto",
@@ -68,7 +80,35 @@ def parse():
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="one-layer workloads: calls timed after writing a 1 GiB scratch "
                          "buffer, which evicts the L2 and the 256 MB MALL (0 = skip)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def default_args():
+    return parse([])
+
+
+# Workloads timed after the headline in a default run: (name, timed steps,
+# warmup steps).  A full step is 32 layers, about 33 ms.
+EXTRA_WORKLOADS = [("batch10", 50, 10), ("shared_prefix", 50, 10), ("full_step", 3, 1),
+                   ("beam_step", 5, 2), ("prefill_prompt", 20, 5), ("prefill_chunked", 20, 5)]
+ONE_LAYER = ("batch10", "shared_prefix", "prefill_prompt", "prefill_chunked")
+
+
+def summarise(rec):
+    """The fields of another workload's record that go into the headline
+    line: its step time and rate, its call time, its roofline, seq-layers/s
+    and its own CPU baseline."""
+    keep = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "seq_layers_per_s",
+            "pa_decode_us", "pa_decode_us_median", "pa_decode_kv_gbs", "pa_decode_pct_hbm_peak",
+            "pa_decode_unique_kv_gbs", "pa_decode_us_cold_median", "pa_prefill_us",
+            "pa_prefill_us_median", "pa_prefill_tflops", "pa_prefill_gbs",
+            "pa_prefill_us_cold_median", "decode", "groups", "layers", "query_rows")
+    out = {"config": rec["config"]}
+    out.update({k: rec[k] for k in keep if k in rec})
+    out["roofline"] = {k: v for k, v in rec["roofline"].items() if k != "traffic"}
+    if "cpu_baseline" in rec:
+        out["cpu_baseline"] = rec["cpu_baseline"]
+    return out
 
 
 def algorithmic_bytes(lens, H, D):
@@ -199,63 +239,187 @@ def _sample_pools(tables, kp, vp, torch):
     return k_small, v_small, rows
 
 
-def cpu_baseline(run, torch, budget_s=15.0, units=0):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    the first sequences (whole groups for the grouped decode; layer 0 of a
-    full step), grown until the oracle takes about ``budget_s`` seconds."""
+# Host threads the CPU baseline may use: the cores this process may run on,
+# at most 16 (the host share of one GPU).
+CPU_WORKERS_MAX = 16
+
+
+def cpu_workers():
+    return max(1, min(len(os.sched_getaffinity(0)), CPU_WORKERS_MAX))
+
+
+def cpu_sample(run, torch):
+    """The oracle's inputs for a bounded sample of the workload, as host
+    arrays: every sequence of a one-layer decode (whole groups for the
+    grouped decode), layer 0 of a full step (the per-step figure is that
+    layer's rate, an extrapolation to the step's layers), all prompts of the
+    prompt prefill, the first 8 sequences of the chunked prefill."""
     import numpy as np
 
     import workloads as wl
-    from oracle import grouped_decode_ref, paged_decode_ref, paged_prefill_ref
     case = run.case
     q_all = case.q[0] if case.q.ndim == 4 else case.q
-    H, D = case.num_heads, case.head_dim
     prefill = getattr(run, "prefill", None) is not None
     grouped = run.extra.get("decode") == "pa_decode_grouped"
-    if grouped:
-        offs, shared = wl.table_groups(case.block_tables, case.context_lens)
-        total = len(shared)
-        n = min(total, units or 1)
-        nseq = int(offs[n])
-        what = f"first {n} of {total} groups, {nseq} sequences"
-    else:
-        total = case.batch
-        nseq = min(total, units or (2 if prefill else 16))   # a prefill sequence costs more
-        n = nseq
-        what = f"first {nseq} of {total} sequences"
-    k_small, v_small, tables = _sample_pools(case.block_tables[:nseq], run.kp, run.vp, torch)
-    lens = case.context_lens[:nseq]
-    w0, c0 = time.perf_counter(), time.process_time()
+    meta = {"scale": float(case.scale), "heads": case.num_heads, "head_dim": case.head_dim,
+            "layers": case.num_layers, "batch": case.batch}
+    arrays = {}
     if prefill:
+        nseq = min(case.batch, 8) if run.chunked else case.batch
         qs = case.query_start[:nseq + 1].astype(np.int64)
-        paged_prefill_ref(q_all[qs[0]:qs[-1]], k_small, v_small, tables, lens, qs - qs[0],
-                          case.scale)
+        arrays["q"] = q_all[qs[0]:qs[-1]]
+        arrays["query_start"] = qs - qs[0]
+        meta.update(kind="prefill", what=f"first {nseq} of {case.batch} sequences")
     elif grouped:
-        grouped_decode_ref(q_all[:nseq], k_small, v_small, tables, lens, offs[:n + 1],
-                           shared[:n], case.scale)
+        offs, shared = wl.table_groups(case.block_tables, case.context_lens)
+        nseq = int(offs[-1])
+        arrays["q"] = q_all[:nseq]
+        arrays["group_offsets"] = offs.astype(np.int64)
+        arrays["shared_blocks"] = shared.astype(np.int64)
+        meta.update(kind="grouped", what=f"all {len(shared)} groups ({nseq} sequences)")
     else:
-        paged_decode_ref(q_all[:nseq], k_small, v_small, tables, lens, case.scale)
-    wall, cpu = time.perf_counter() - w0, time.process_time() - c0
-    if not units and wall < budget_s / 4 and n < total:
-        # scale the sample up to roughly the budget, within the workload
-        more = min(total, int(n * budget_s / max(wall, 1e-3)))
-        return cpu_baseline(run, torch, budget_s, units=max(more, n + 1))
-    tokens = int(lens.astype(np.int64).sum())
-    rec = {"cores": max(1, round(cpu / wall)), "kind": "oracle"}
-    layer = ", layer 0 of the step" if case.q.ndim == 4 else ", one layer"
-    if prefill:
-        rows = int(case.query_start[nseq] - case.query_start[0])
-        rec.update(value=rows / wall, unit="tokens/s",
-                   sample=f"{what} ({rows} query rows over {tokens} context tokens){layer}, "
-                          f"float64 numpy oracle, {wall:.1f} s wall")
+        nseq = case.batch
+        arrays["q"] = q_all[:nseq]
+        meta.update(kind="decode", what=f"all {nseq} sequences")
+    k_small, v_small, tables = _sample_pools(case.block_tables[:nseq], run.kp, run.vp, torch)
+    arrays.update(k_pool=k_small, v_pool=v_small, tables=tables,
+                  lens=case.context_lens[:nseq].astype(np.int64))
+    meta["layer"] = "layer 0 of the step" if case.q.ndim == 4 else "one layer"
+    return arrays, meta
+
+
+def cpu_baseline(run, torch):
+    """The oracle, as it stands, timed on the host's cores on a bounded
+    sample of the workload (``cpu_sample``).  It runs in a child process
+    that never touches the GPU: the sample goes through .npy files, and the
+    child spreads the oracle's work units (sequences, groups, or row ranges
+    of a prefill) over a pool of forked workers with one BLAS thread each;
+    a serial pass over a few units gives the single-core rate."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
+    arrays, meta = cpu_sample(run, torch)
+    tmp = tempfile.mkdtemp(prefix="pkv_cpu_baseline_")
+    try:
+        for name, a in arrays.items():
+            np.save(os.path.join(tmp, name + ".npy"), np.ascontiguousarray(a))
+        with open(os.path.join(tmp, "meta.json"), "w") as f:
+            json.dump(meta, f)
+        del arrays
+        env = dict(os.environ)
+        for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+            env[var] = "1"
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-worker", tmp],
+                             env=env, stdout=subprocess.PIPE, timeout=600, check=True, text=True)
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+# -- the CPU-baseline child process (no GPU) ---------------------------------
+
+_W = {}
+
+
+def _unit_work(i):
+    """Run work unit i of the sample through the oracle; returns its wall
+    seconds."""
+    import numpy as np
+    from oracle import paged_decode_ref, paged_prefill_ref
+    a, meta, (lo, hi, r0, r1) = _W["arrays"], _W["meta"], _W["units"][i]
+    t0 = time.perf_counter()
+    if meta["kind"] == "prefill":
+        qs = a["query_start"]
+        n = int(qs[lo + 1] - qs[lo])
+        ctx = int(a["lens"][lo])
+        # rows r0 .. r1-1 of sequence lo: the same positions as a query set
+        # of r1 - r0 rows over the context up to row r1 - 1
+        rows = np.arange(qs[lo] + r0, qs[lo] + r1)
+        paged_prefill_ref(a["q"][rows], a["k_pool"], a["v_pool"], a["tables"][lo:lo + 1],
+                          np.array([max(ctx - n + r1, 0)]), np.array([0, r1 - r0]),
+                          meta["scale"])
+    elif meta["kind"] == "grouped":
+        # sequences lo .. hi-1 with the tables and lengths the grouping
+        # contract gives them (grouped_tables_ref, applied once to the sample)
+        paged_decode_ref(a["q"][lo:hi], a["k_pool"], a["v_pool"], _W["g_tables"][lo:hi],
+                         _W["g_lens"][lo:hi], meta["scale"])
     else:
-        rec.update(value=tokens * 2 * H * D * 2 / wall / 1e9, unit="GB/s",
-                   seq_layers_per_s=nseq / wall,
-                   sample=f"{what} ({tokens} context tokens){layer}, float64 numpy oracle"
-                          + (" under the grouping contract" if grouped else "")
-                          + f", {wall:.1f} s wall")
-    return {k: rec[k] for k in ("value", "unit", "cores", "kind", "sample")} | \
-        {k: v for k, v in rec.items() if k not in ("value", "unit", "cores", "kind", "sample")}
+        paged_decode_ref(a["q"][lo:hi], a["k_pool"], a["v_pool"], a["tables"][lo:hi],
+                         a["lens"][lo:hi], meta["scale"])
+    return time.perf_counter() - t0
+
+
+def cpu_worker_main(tmp):
+    """Child process: load the sample, time the oracle serially on a few
+    units (single core), then on all units over the worker pool; print one
+    JSON object."""
+    import multiprocessing as mp
+
+    import numpy as np
+    with open(os.path.join(tmp, "meta.json")) as f:
+        meta = json.load(f)
+    arrays = {n[:-4]: np.load(os.path.join(tmp, n), mmap_mode="r")
+              for n in os.listdir(tmp) if n.endswith(".npy")}
+    H, D = meta["heads"], meta["head_dim"]
+    workers = cpu_workers()
+    lens = np.asarray(arrays["lens"], dtype=np.int64)
+    units, work = [], []               # (lo, hi, r0, r1), and its measure
+    if meta["kind"] == "prefill":
+        qs = np.asarray(arrays["query_start"])
+        rows_total = int(qs[-1])
+        per = max(1, -(-rows_total // (4 * workers)))   # rows per unit
+        for b in range(len(lens)):
+            n = int(qs[b + 1] - qs[b])
+            for r0 in range(0, n, per):
+                units.append((b, b + 1, r0, min(n, r0 + per)))
+                work.append(min(n, r0 + per) - r0)
+        unit, scale = "tokens/s", 1.0
+    else:
+        per = max(1, -(-len(lens) // (4 * workers)))
+        for lo in range(0, len(lens), per):
+            units.append((lo, min(len(lens), lo + per), 0, 0))
+            work.append(int(lens[lo:lo + per].sum()))
+        unit, scale = "GB/s", 2 * H * D * 2 / 1e9
+    _W.update(arrays=arrays, meta=meta, units=units)
+    t_groups = 0.0
+    if meta["kind"] == "grouped":
+        # the grouping contract once (host work, timed and added to both
+        # figures); the decode of its tables is split into sequence units
+        from oracle import grouped_tables_ref
+        t0 = time.perf_counter()
+        g_tables, g_lens = grouped_tables_ref(arrays["tables"], lens, arrays["group_offsets"],
+                                              arrays["shared_blocks"], 16)
+        t_groups = time.perf_counter() - t0
+        _W.update(g_tables=g_tables, g_lens=g_lens)
+    # single core: units in order until about 3 s have passed
+    t_one, w_one, n_one = t_groups, 0, 0
+    for i in range(len(units)):
+        t_one += _unit_work(i)
+        w_one += work[i]
+        n_one += 1
+        if t_one >= 3.0:
+            break
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(int, range(workers))               # workers up before the clock starts
+        t0 = time.perf_counter()
+        pool.map(_unit_work, range(len(units)), chunksize=1)
+        wall = time.perf_counter() - t0 + t_groups
+    total = sum(work)
+    seqs = len(lens)
+    rec = {"value": total * scale / wall, "unit": unit, "cores": workers, "kind": "oracle",
+           "sample": f"{meta['what']} ({total} {'query rows' if unit == 'tokens/s' else 'context tokens'}"
+                     f"), {meta['layer']}, float64 numpy oracle in {len(units)} work units over "
+                     f"{workers} worker processes (1 BLAS thread each), {wall:.2f} s wall",
+           "single_core": {"value": w_one * scale / t_one, "unit": unit,
+                           "sample": f"first {n_one} of {len(units)} work units, one process, "
+                                     f"{t_one:.2f} s"},
+           "host_cpus_visible": len(os.sched_getaffinity(0))}
+    if unit == "GB/s":
+        rec["seq_layers_per_s"] = seqs / wall
+    print(json.dumps(rec), flush=True)
 
 
 class Run:
@@ -638,6 +802,7 @@ def setup_prefill(torch, dev, wl, args, chunked):
     rows = int(n.sum())
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=case.batch, kv_bytes=kv_bytes,
                algo_bytes=kv_bytes + io_bytes + write_bytes, strategy="prefill", part=0,
+               chunked=chunked,
                prefill={"rows": rows, "flops": flops, "pairs": pairs,
                         "kernel": "pa_prefill_append" if fused else "pa_prefill"},
                extra={"query_rows": rows, "causal_pairs": pairs},
@@ -653,72 +818,54 @@ def setup_prefill(torch, dev, wl, args, chunked):
                        "seed": case.meta["seed"]})
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        write_traffic_record(*args.traffic_from)
-        return
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; the library runs on one GPU "
-              "(there is no multi-GPU path).", file=sys.stderr)
-        sys.exit(2)
+def measure(torch, dev, wl, args, name, steps, warmup, cold_reps=0, probe=False, cpu=True):
+    """Set up workload ``name``, run ``warmup`` untimed steps and ``steps``
+    timed ones, and return its bench record (without printing it)."""
     import numpy as np
-    import torch
 
-    import workloads as wl
-    from paged_kv_cache_03_amd import load_library
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    load_library()   # fails loudly when the HIP library is not built
-    dev = torch.device("cuda:0")
-    log(f"device {torch.cuda.get_device_name(0)} "
-        f"({torch.cuda.get_device_properties(0).gcnArchName})")
-
-    if args.workload == "batch200":
+    if name == "batch200":
         run = setup_batch(torch, dev, wl, args, 200, 2)
-    elif args.workload == "batch10":
+    elif name == "batch10":
         run = setup_batch(torch, dev, wl, args, 10, 1)
-    elif args.workload == "shared_prefix":
+    elif name == "shared_prefix":
         run = setup_shared_prefix(torch, dev, wl, args)
-    elif args.workload == "vattention":
+    elif name == "vattention":
         run = setup_vattention(torch, dev, wl, args)
-    elif args.workload.startswith("prefill"):
-        run = setup_prefill(torch, dev, wl, args, args.workload == "prefill_chunked")
+    elif name.startswith("prefill"):
+        run = setup_prefill(torch, dev, wl, args, name == "prefill_chunked")
     else:
-        run = setup_full_step(torch, dev, wl, args, 4 if args.workload == "beam_step" else 1)
-    log(f"workload {args.workload}: {run.config}")
+        run = setup_full_step(torch, dev, wl, args, 4 if name == "beam_step" else 1)
+    log(f"workload {name}: {run.config}")
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         run.step([])
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
+    log(f"warmup {warmup} done")
 
     events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         run.step(events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+    log(f"timed {steps} steps in {elapsed * 1e3:.2f} ms")
     dec_ms = [events[i].elapsed_time(events[i + 1]) for i in range(0, len(events), 2)]
     dec_avg_s = float(np.mean(dec_ms)) / 1e3
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / steps
 
     step_gbs = run.kv_bytes / (ms_per_step / 1e3) / 1e9
-    kv_per_call = run.kv_bytes / (len(dec_ms) / args.steps)
+    kv_per_call = run.kv_bytes / (len(dec_ms) / steps)
     dec_gbs = kv_per_call / dec_avg_s / 1e9
     achieved = run.algo_bytes / dec_avg_s / 1e9
-    headline = args.workload == "batch200" and getattr(run, "fused", False)
+    headline = name == "batch200" and getattr(run, "fused", False)
     result = {
         "metric": "pa_decode K/V GB/s (% MI355X HBM peak) + seq-layers/s at batch 200",
         "value": round(step_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -736,6 +883,8 @@ def main():
         "roofline": {
             "kernel": ("pa_decode_append (fused append + decode kernel, merge kernel; one call)"
                        if getattr(run, "fused", False) else
+                       "pa_decode_grouped (grouped decode + merge kernels, one call)"
+                       if run.extra.get("decode") == "pa_decode_grouped" else
                        "pa_decode (decode + merge kernels, one call)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -770,7 +919,7 @@ def main():
                                       flops_per_launch=pf["flops"])
         else:
             result["roofline"].update(kernel=pf["kernel"])
-    if "unique_kv_bytes" in run.extra:      # per decode call: each distinct block once
+    if run.extra.get("unique_kv_bytes", kv_per_call) < kv_per_call:   # each distinct block once
         result["pa_decode_unique_kv_gbs"] = round(run.extra["unique_kv_bytes"] / dec_avg_s / 1e9, 2)
         # blocks shared by several sequences: HBM sees each once, so the
         # roofline counts the distinct blocks (the logical rate stays above)
@@ -781,7 +930,7 @@ def main():
             frac=round(unique_call / dec_avg_s / 1e9 / HBM_PEAK_GBS, 4),
             bytes_per_launch=int(unique_call), logical_bytes_per_launch=run.algo_bytes)
 
-    if args.cold_reps > 0 and args.workload in ("batch200", "batch10", "shared_prefix",
+    if cold_reps > 0 and name in ("batch200", "batch10", "shared_prefix",
                                                 "vattention", "prefill_prompt",
                                                 "prefill_chunked"):
         # The timed steps above run warm: a working set under 256 MB (batch 10)
@@ -789,7 +938,7 @@ def main():
         # steps.  Here every call starts after 1 GiB of unrelated writes.
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         cold = []
-        for i in range(args.cold_reps):
+        for i in range(cold_reps):
             scratch.fill_(i & 0xFF)
             ev = []
             run.step(ev)
@@ -799,13 +948,13 @@ def main():
         key = "pa_prefill" if pf is not None else "pa_decode"
         result[key + "_us_cold_median"] = round(float(np.median(cold)) * 1e3, 3)
         result[key + "_us_cold_p90"] = round(float(np.percentile(cold, 90)) * 1e3, 3)
-        result[key + "_cold_reps"] = args.cold_reps
+        result[key + "_cold_reps"] = cold_reps
 
-    if not args.no_hbm_probe and args.workload == "batch200":
-        probe = hbm_probe(torch, dev)
-        result["hbm_probe"] = probe
-        result["roofline"]["achievable_gather_gbs"] = probe["gather_4k_gbs"]
-        result["roofline"]["frac_of_achievable"] = round(achieved / probe["gather_4k_gbs"], 4)
+    if probe:
+        hp = hbm_probe(torch, dev)
+        result["hbm_probe"] = hp
+        result["roofline"]["achievable_gather_gbs"] = hp["gather_4k_gbs"]
+        result["roofline"]["frac_of_achievable"] = round(achieved / hp["gather_4k_gbs"], 4)
 
     if args.copy_probe:
         n = 1 << 30
@@ -824,10 +973,54 @@ def main():
                                 "gbs_read_plus_write": round(2 * n / t / 1e9, 1)}
         del src, dst
 
-    if not args.no_cpu_baseline:
-        log("timing the oracle on a sample of the workload (cpu baseline)")
-        result["cpu_baseline"] = cpu_baseline(run, torch, units=args.cpu_seqs)
+    if cpu:
+        log(f"{name}: timing the oracle on a sample of the workload (cpu baseline)")
+        result["cpu_baseline"] = cpu_baseline(run, torch)
         log(f"cpu baseline: {result['cpu_baseline']['sample']}")
+    del run
+    return result
+
+
+def main():
+    args = parse()
+    if args.cpu_worker:
+        cpu_worker_main(args.cpu_worker)
+        return
+    if args.traffic_from:
+        write_traffic_record(*args.traffic_from)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; the library runs on one GPU "
+              "(there is no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_03_amd import load_library
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    load_library()   # fails loudly when the HIP library is not built
+    dev = torch.device("cuda:0")
+    log(f"device {torch.cuda.get_device_name(0)} "
+        f"({torch.cuda.get_device_properties(0).gcnArchName})")
+
+    headline = args.workload == "batch200"
+    result = measure(torch, dev, wl, args, args.workload, args.steps, args.warmup,
+                     cold_reps=args.cold_reps, probe=headline and not args.no_hbm_probe,
+                     cpu=not args.no_cpu_baseline)
+    if headline and not args.no_extras:
+        # the other workloads, each timed in the same run and summarised
+        # inside the one line
+        result["other_workloads"] = {}
+        for name, steps, warmup in EXTRA_WORKLOADS:
+            torch.cuda.empty_cache()
+            rec = measure(torch, dev, wl, default_args(), name, steps, warmup,
+                          cold_reps=args.cold_reps if name in ONE_LAYER else 0,
+                          cpu=not args.no_cpu_baseline)
+            result["other_workloads"][name] = summarise(rec)
+            log(f"{name}: {json.dumps(result['other_workloads'][name]['roofline'])}")
     print(json.dumps(result), flush=True)
 
 

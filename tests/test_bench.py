@@ -76,3 +76,34 @@ def test_full_step_bytes_match_the_pages_per_token_figure():
                 for _ in range(c.num_layers))
     assert kv_bytes_per_token(32, 32, 128) == per_token == 524288
     assert total == 200 * 2048 * kv_bytes_per_token(32, 32, 128) == 214_748_364_800
+
+
+def _host_run(case, **extra):
+    import torch
+    return bench.Run(case=case, kp=torch.from_numpy(case.k_pool), vp=torch.from_numpy(case.v_pool),
+                     extra=extra.pop("extra", {}), **extra)
+
+
+def test_cpu_baseline_runs_the_oracle_over_a_worker_pool():
+    """The CPU-baseline leg end to end on the host: the sample is written
+    out, a child process times the oracle serially (single core) and over a
+    pool of forked workers, for a decode, a grouped decode and a prefill
+    sample; the record names the core count and both rates."""
+    import torch
+
+    import workloads as wl
+    cases = [
+        (_host_run(wl.gpt_batch(12, seed=1, append=True, num_blocks=1024, heads=4, head_dim=64)),
+         "GB/s"),
+        (_host_run(wl.shared_prefix(batch=6, seed=7, prefix_tokens=40, suffix_max=50, heads=4,
+                                    head_dim=64), extra={"decode": "pa_decode_grouped"}), "GB/s"),
+        (_host_run(wl.prefill(5, seed=3, heads=4, head_dim=64), prefill={"rows": 0},
+                   chunked=False), "tokens/s"),
+    ]
+    for run, unit in cases:
+        rec = bench.cpu_baseline(run, torch)
+        assert rec["kind"] == "oracle" and rec["unit"] == unit
+        assert rec["cores"] == bench.cpu_workers() >= 1
+        assert rec["value"] > 0 and rec["single_core"]["value"] > 0
+        assert rec["single_core"]["unit"] == unit
+        assert "worker processes" in rec["sample"]
