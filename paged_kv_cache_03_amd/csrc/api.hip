@@ -120,7 +120,8 @@ GroupPlan make_group_plan(int32_t B, int32_t H, int32_t D, int32_t max_ctx, int3
   GroupPlan p;
   const long long hg = (H + pkv::kGroupWaves - 1) / pkv::kGroupWaves;
   const long long t_max = (long long)B * ceil_div(max_ctx, kBlockTokens);
-  const long long cap = ((long long)pkv::kGroupMaxLdsBytes / 4 - G - 1) / 4;   // positions
+  // LDS: B context lengths, G + 1 group offsets, 4 ints a position
+  const long long cap = ((long long)pkv::kGroupMaxLdsBytes / 4 - B - G - 1) / 4;   // positions
   if (cap <= 0) return p;
   long long nr = pkv::kGroupGridTarget / hg > 0 ? pkv::kGroupGridTarget / hg : 1;
   if ((t_max + nr - 1) / nr > cap) nr = (t_max + cap - 1) / cap;

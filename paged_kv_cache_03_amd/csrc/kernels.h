@@ -110,7 +110,7 @@ constexpr int kGroupTiles = 3;             // tiles in each wave's load ring
 #define PKV_GROUP_GRID 512
 #endif
 constexpr int kGroupGridTarget = PKV_GROUP_GRID;   // workgroups (ranges x head groups) at least
-constexpr int kGroupMaxLdsBytes = 44 * 1024;       // dynamic LDS: group offsets + range staging
+constexpr int kGroupMaxLdsBytes = 44 * 1024;       // dynamic LDS: contexts, group offsets, range staging
                                                    // (with the 16 KiB V staging: under 64 KiB)
 
 struct GroupArgs {
@@ -199,7 +199,7 @@ hipError_t launch_hbm_read_probe(const void* buf, long long n16, uint32_t* sink,
 hipError_t launch_hbm_gather_probe(const void* buf, const int32_t* order, long long n_chunks,
                                    int log_kib, uint32_t* sink, int grid, hipStream_t stream);
 hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, hipStream_t stream);
-size_t grouped_lds_bytes(int G, int max_chunk);
+size_t grouped_lds_bytes(int B, int G, int max_chunk);
 hipError_t launch_pa_prefill(const PrefillArgs& a, int D, int grid, int max_blocks_used,
                              hipStream_t stream);
 hipError_t launch_pa_prefill_append(const PrefillArgs& a, int D, int grid, int max_blocks_used,

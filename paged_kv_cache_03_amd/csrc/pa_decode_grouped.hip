@@ -54,12 +54,16 @@ __device__ __forceinline__ void group_members(const GroupArgs& a, int g, int& lo
   n = clampi(hi - lo, 0, a.group_size);
 }
 
-__device__ GroupShape group_shape(const GroupArgs& a, int g) {
+// s_ctx: every sequence's context length, clamped to [0, ctx_limit],
+// staged in LDS once per workgroup (one load per thread), so that the
+// member loops below read LDS rather than a chain of dependent global
+// loads.
+__device__ GroupShape group_shape(const GroupArgs& a, const int* s_ctx, int g) {
   GroupShape s;
   group_members(a, g, s.lo, s.n);
   int sum_nb = 0, min_full = 1 << 30;
   for (int k = 0; k < s.n; ++k) {
-    const int ctx = clampi(a.context_lens[s.lo + k], 0, a.ctx_limit);
+    const int ctx = s_ctx[s.lo + k];
     sum_nb += (ctx + kBlockTokens - 1) / kBlockTokens;
     min_full = min(min_full, ctx / kBlockTokens);
   }
@@ -75,11 +79,11 @@ struct PosInfo {
   int row, j, member, valid;
 };
 
-__device__ PosInfo position_info(const GroupArgs& a, const GroupShape& gs, int pos) {
+__device__ PosInfo position_info(const int* s_ctx, const GroupShape& gs, int pos) {
   if (pos < gs.shared) return {gs.lo, pos, kInfoShared, kBlockTokens};
   int start = gs.shared;               // member k's private blocks start here
   for (int k = 0; k < gs.n; ++k) {
-    const int ctx = clampi(a.context_lens[gs.lo + k], 0, a.ctx_limit);
+    const int ctx = s_ctx[gs.lo + k];
     const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
     const int own = nb - gs.shared;
     if (pos < start + own) {
@@ -97,7 +101,8 @@ __device__ PosInfo position_info(const GroupArgs& a, const GroupShape& gs, int p
 // disjoint under the contract, so the total stays below it, but overlapping
 // groups in device data must not push a range past its LDS staging.  All
 // threads take part; ends with a barrier.
-__device__ void position_prefix(const GroupArgs& a, int* s_gpos, long long* s_wave) {
+__device__ void position_prefix(const GroupArgs& a, const int* s_ctx, int* s_gpos,
+                                long long* s_wave) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int per = (a.G + nt - 1) / nt;
@@ -105,7 +110,7 @@ __device__ void position_prefix(const GroupArgs& a, int* s_gpos, long long* s_wa
   const int hi = min(a.G, lo + per);
   long long own = 0;
   for (int g = lo; g < hi; ++g) {
-    const int np = group_shape(a, g).npos;
+    const int np = group_shape(a, s_ctx, g).npos;
     s_gpos[g] = np;                    // counts first, offsets below
     own += np;
   }
@@ -150,7 +155,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
   extern __shared__ int smem[];
   __shared__ long long s_wave[kGroupWaves];
   __shared__ u4v s_v[kGroupWaves][kK * kWave];   // each wave's V tile, as loaded
-  int* s_gpos = smem;                  // G + 1
+  int* s_ctx = smem;                   // B: context lengths, clamped
+  int* s_gpos = s_ctx + a.B;           // G + 1
   int* s_id = s_gpos + a.G + 1;        // max_chunk: block id of each position of the range
   int* s_info = s_id + a.max_chunk;    // max_chunk: member | valid << 8
   int* s_grp = s_info + a.max_chunk;   // max_chunk: group of each position
@@ -165,7 +171,9 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
   const int r = blockIdx.x / a.head_groups;
   const int h = hg * kGroupWaves + wave;
 
-  position_prefix(a, s_gpos, s_wave);
+  for (int b = tid; b < a.B; b += blockDim.x) s_ctx[b] = clampi(a.context_lens[b], 0, a.ctx_limit);
+  __syncthreads();
+  position_prefix(a, s_ctx, s_gpos, s_wave);
   if (blockIdx.x == 0) {
     // group offsets and the per-sequence map (group * 16 + member, or -1)
     // for the merge
@@ -188,8 +196,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
   for (int i = tid; i < cnt; i += blockDim.x) {
     const int s = c0 + i;
     const int g = group_of(s_gpos, a.G, s);
-    const GroupShape gs = group_shape(a, g);
-    const PosInfo pi = position_info(a, gs, s - s_gpos[g]);
+    const GroupShape gs = group_shape(a, s_ctx, g);
+    const PosInfo pi = position_info(s_ctx, gs, s - s_gpos[g]);
     const int id = a.block_tables[(size_t)pi.row * a.max_blocks + pi.j];
     s_id[i] = clampi(id, 0, a.num_blocks - 1);
     s_info[i] = pi.member | (pi.valid << 8);
@@ -234,12 +242,15 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
     // would hold back one tile in every round of the ring.
     __builtin_amdgcn_sched_barrier(0);
 
+    // V tokens at or past the position's valid count load as zeros
     auto fetch = [&](MTile<D>& t, int j) {
       const int jj = sg + min(j, scnt - 1);
       const uint32_t bytes = j < scnt ? kTile : 0u;
       const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_id[jj]) * block_stride;
+      const int valid = __builtin_amdgcn_readfirstlane(s_info[jj]) >> 8;
+      const uint32_t v_off = lane % kBlockTokens < valid ? lane_off : 0xFFFFF000u;
       mfma_fetch<D, kPolicy>(t, make_rsrc(kbase + o, bytes), make_rsrc(vbase + o, bytes),
-                             lane_off);
+                             lane_off, v_off);
     };
 
     float m = kNegInf, l = 0.0f;       // for query qc; l over this lane's tokens only
@@ -256,8 +267,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
       const int member = info & 0xff;
       const int valid = info >> 8;
       const bool qok = qc < n && (member == kInfoShared || qc == member - 1);
-      mfma_update<D>(t, qb, a.scale_log2, valid, [&](int tok) { return qok && tok < valid; }, m,
-                     l, acc, sv, svh, lane);
+      mfma_update<D>(t, qb, a.scale_log2, [&](int tok) { return qok && tok < valid; }, m, l,
+                     acc, sv, svh, lane);
     };
 
     // (a do-while: a segment is never empty, and a ring entered only when
@@ -292,28 +303,50 @@ __global__ __launch_bounds__(64 * kGroupWaves) void pa_decode_grouped_kernel(Gro
           *reinterpret_cast<h4v*>(orow + 16 * s) = o;
         }
       } else {
+        // (m, l) for every member; the weighted sums only for a member that
+        // met a live token here (m > -inf): the merge skips the others'
         const size_t piece =
             (((size_t)h * a.nr + r) * 2 + (seg_lo > gstart ? 0 : 1)) * a.group_size + qc;
         if (tg == 0) {
           a.ws_ml[piece * 2] = m;
           a.ws_ml[piece * 2 + 1] = l;
         }
-        f4v* dst = reinterpret_cast<f4v*>(a.ws_acc + piece * D);
+        if (m != kNegInf) {
+          f4v* dst = reinterpret_cast<f4v*>(a.ws_acc + piece * D);
 #pragma unroll
-        for (int s = 0; s < kS; ++s) dst[4 * s + tg] = acc[s];
+          for (int s = 0; s < kS; ++s) dst[4 * s + tg] = acc[s];
+        }
       }
     }
     sg += scnt;
   }
 }
 
+// Sum over the wave (every lane ends with the total, the same in every
+// lane).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) x += __shfl_xor(x, d, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) x = fmaxf(x, __shfl_xor(x, d, kWave));
+  return x;
+}
+
 // One wave per (sequence, head): zero row for a sequence that is in no
 // group or has nothing to attend to; for a member of a group cut across
-// ranges, combine its partials in range order (weights exp2(m_r - M));
-// otherwise nothing (the decode kernel wrote the row).
+// ranges, combine its partials (weights exp2(m_r - M)); otherwise nothing
+// (the decode kernel wrote the row).  A group can span many ranges, so the
+// pieces' (m, l) are read one per lane, at once, and the weighted sums of
+// eight pieces are loaded before they are added; a piece whose m is -inf
+// (no live token of the member in that range) has no weighted sums and is
+// left out by a select, so no stale value is ever multiplied.
 template <int D>
 __global__ __launch_bounds__(256) void pa_decode_grouped_merge_kernel(GroupArgs a) {
   constexpr int kPer = D / kWave;
+  constexpr int kUnroll = 8;
   const int lane = threadIdx.x % kWave;
   const int bh = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (bh >= a.B * a.H) return;
@@ -339,20 +372,49 @@ __global__ __launch_bounds__(256) void pa_decode_grouped_merge_kernel(GroupArgs 
   auto piece = [&](int rr) {
     return (((size_t)h * a.nr + rr) * 2 + (rr * chunk > S ? 0 : 1)) * a.group_size + k;
   };
+  // the largest reference over all pieces, 64 pieces a round
   float mx = kNegInf;
-  for (int rr = r0; rr <= r1; ++rr) mx = fmaxf(mx, a.ws_ml[piece(rr) * 2]);
+  for (int base = r0; base <= r1; base += kWave) {
+    const int rr = base + lane;
+    if (rr <= r1) mx = fmaxf(mx, a.ws_ml[piece(rr) * 2]);
+  }
+  mx = wave_max(mx);
   if (mx == kNegInf) return zero_row();   // a member with no tokens
   float den = 0.0f;
   float num[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) num[e] = 0.0f;
-  for (int rr = r0; rr <= r1; ++rr) {
-    const size_t pc = piece(rr);
-    const float w = exp2f(a.ws_ml[pc * 2] - mx);
-    den = fmaf(w, a.ws_ml[pc * 2 + 1], den);
+  for (int base = r0; base <= r1; base += kWave) {
+    const int rr = base + lane;
+    float w = 0.0f;                    // this lane's piece's weight, 0 if empty
+    if (rr <= r1) {
+      const size_t pc = piece(rr);
+      const float mr = a.ws_ml[pc * 2];
+      if (mr != kNegInf) {
+        w = exp2f(mr - mx);
+        den = fmaf(w, a.ws_ml[pc * 2 + 1], den);
+      }
+    }
+    const int cnt = min(kWave, r1 - base + 1);
+    for (int j0 = 0; j0 < cnt; j0 += kUnroll) {
+      float acc_j[kUnroll][kPer];
+      float w_j[kUnroll];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) num[e] = fmaf(w, a.ws_acc[pc * D + lane * kPer + e], num[e]);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = min(j0 + u, cnt - 1);
+        w_j[u] = j0 + u < cnt ? __shfl(w, j, kWave) : 0.0f;
+        const float* src = a.ws_acc + piece(base + j) * D + lane * kPer;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc_j[u][e] = src[e];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          num[e] = w_j[u] != 0.0f ? fmaf(w_j[u], acc_j[u][e], num[e]) : num[e];
+    }
   }
+  den = wave_sum(den);
   const float inv = 1.0f / den;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) orow[lane * kPer + e] = (_Float16)(num[e] * inv);
@@ -360,12 +422,12 @@ __global__ __launch_bounds__(256) void pa_decode_grouped_merge_kernel(GroupArgs 
 
 }  // namespace
 
-size_t grouped_lds_bytes(int G, int max_chunk) {
-  return ((size_t)G + 1 + 4 * (size_t)max_chunk) * sizeof(int);
+size_t grouped_lds_bytes(int B, int G, int max_chunk) {
+  return ((size_t)B + G + 1 + 4 * (size_t)max_chunk) * sizeof(int);
 }
 
 hipError_t launch_pa_decode_grouped(const GroupArgs& a, int D, hipStream_t stream) {
-  const size_t lds = grouped_lds_bytes(a.G, a.max_chunk);
+  const size_t lds = grouped_lds_bytes(a.B, a.G, a.max_chunk);
   const int threads = kWave * kGroupWaves;
   const int grid = a.head_groups * a.nr;
   if (D == 128 && !a.keep_cached)

@@ -276,10 +276,12 @@ def test_grouped_workspace_size():
     assert ws(200, 64, 128, 2048, 50, 4) == base
     assert ws(200, 32, 128, 4096, 50, 4) == base
     assert ws(200, 32, 64, 2048, 50, 4) < base
-    # the group offsets are staged on chip next to at least one position of
-    # range staging: 11,259 groups are the most a call takes
-    assert ws(8, 32, 128, 2048, 11259, 16) > 0
-    assert ws(8, 32, 128, 2048, 11260, 16) == 0
+    # the context lengths and group offsets are staged on chip next to at
+    # least one position of range staging: B + num_groups is at most 11,259
+    assert ws(8, 32, 128, 2048, 11251, 16) > 0
+    assert ws(8, 32, 128, 2048, 11252, 16) == 0
+    assert ws(5000, 32, 128, 2048, 6259, 16) > 0
+    assert ws(5000, 32, 128, 2048, 6260, 16) == 0
 
 
 def test_prefill_rejects_bad_arguments(lib):
