@@ -102,6 +102,7 @@ def summarise(rec):
             "pa_decode_us", "pa_decode_us_median", "pa_decode_kv_gbs", "pa_decode_pct_hbm_peak",
             "pa_decode_unique_kv_gbs", "pa_decode_us_cold_median", "pa_prefill_us",
             "pa_prefill_us_median", "pa_prefill_tflops", "pa_prefill_gbs",
+            "pa_decode_us_back_to_back", "pa_prefill_us_back_to_back",
             "pa_prefill_us_cold_median", "decode", "groups", "layers", "query_rows")
     out = {"config": rec["config"]}
     out.update({k: rec[k] for k in keep if k in rec})
@@ -479,7 +480,10 @@ def setup_batch(torch, dev, wl, args, batch, seed):
            if fused else "kv_append of 1 token/sequence + pa_decode per step")
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
                algo_bytes=algo_bytes, strategy=strategy, part=part, extra={}, fused=fused,
-               timed_calls=1 if fused else 0,
+               timed_calls=1 if fused else 0, calls_per_call=1,
+               call=None if fused else (lambda: pa_decode(q, kp, vp, tables, lens, case.scale, out,
+                                                          max_context_len=max_ctx, workspace=ws,
+                                                          partition_tokens=part)),
                config={"workload": f"one layer, batch {B}, 32 heads x 128 dims fp16, 16-token "
                                    "blocks, contexts prompt U[32,256] + geometric(mean 500) "
                                    f"capped at 2048, {how}",
@@ -547,6 +551,7 @@ def setup_shared_prefix(torch, dev, wl, args):
 
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=B, kv_bytes=kv_bytes,
                algo_bytes=algo_bytes, strategy=strategy, part=args.partition, extra=extra,
+               call=lambda: decode(q, kp, vp, tables, lens, out), calls_per_call=1,
                config={"workload": "one layer, batch 100, a 1024-token prefix in 64 shared "
                                    "blocks + private suffix U[0,500]; per step copy-on-write of "
                                    "the prefix's last block for each sequence + decode",
@@ -611,9 +616,15 @@ def setup_full_step(torch, dev, wl, args, beams):
                 decode(qs[l], kp, vp, tables, lens, out)
             mark(torch, events)
 
+    def call():                        # every layer's decode alone, back to back
+        for l in range(L):
+            kp, vp = layer_pools[l]
+            decode(qs[l], kp, vp, tables, lens, out)
+
     import numpy as np
     used = np.unique(case.block_tables)
     return Run(case=case, kp=pools[0][0], vp=pools[0][1], step=step, seqs_per_step=B * L,
+               call=None if fused else call, calls_per_call=L,
                kv_bytes=kv_layer * L, algo_bytes=algo_layer, fused=fused,
                timed_calls=L if fused and pairs is None else 0,
                strategy="grouped" if grouped else "flat" if not args.partition else "partitioned",
@@ -801,6 +812,9 @@ def setup_prefill(torch, dev, wl, args, chunked):
     return Run(case=case, kp=kp, vp=vp, step=step, seqs_per_step=case.batch, kv_bytes=kv_bytes,
                algo_bytes=kv_bytes + io_bytes + write_bytes, strategy="prefill", part=0,
                chunked=chunked, timed_calls=1 if fused else 0,
+               call=None if fused else (lambda: pa_prefill(q, kp, vp, tables, lens, qs, case.scale,
+                                                           out, max_context_len=max_ctx)),
+               calls_per_call=1,
                prefill={"rows": rows, "flops": flops, "pairs": pairs,
                         "kernel": "pa_prefill_append" if fused else "pa_prefill"},
                extra={"query_rows": rows, "causal_pairs": pairs},
@@ -908,6 +922,20 @@ def measure(torch, dev, wl, args, name, steps, warmup, cold_reps=0, probe=False,
     }
     if only:      # one average over all calls: no per-call spread
         del result["pa_decode_us_median"], result["pa_decode_us_p90"]
+    elif getattr(run, "call", None) is not None:
+        # The timed call alone, repeated back to back between one event pair
+        # (the step's other kernels and the per-call events left out): the
+        # call's own rate, next to the in-step figure the roofline uses.
+        for _ in range(3):
+            run.call()
+        reps = max(steps, 5)
+        first.record()
+        for _ in range(reps):
+            run.call()
+        last.record()
+        torch.cuda.synchronize()
+        b2b_s = first.elapsed_time(last) / 1e3 / (reps * run.calls_per_call)
+        result["pa_decode_us_back_to_back"] = round(b2b_s * 1e6, 3)
     result.update(run.extra)
     pf = getattr(run, "prefill", None)
     if pf is not None:
@@ -922,6 +950,8 @@ def measure(torch, dev, wl, args, name, steps, warmup, cold_reps=0, probe=False,
         if not only:
             result["pa_prefill_us_median"] = result.pop("pa_decode_us_median")
             result["pa_prefill_us_p90"] = result.pop("pa_decode_us_p90")
+        if "pa_decode_us_back_to_back" in result:
+            result["pa_prefill_us_back_to_back"] = result.pop("pa_decode_us_back_to_back")
         result["pa_prefill_tflops"] = round(tflops, 2)
         result["pa_prefill_gbs"] = round(achieved, 2)
         for k in ("pa_decode_kv_gbs", "pa_decode_pct_hbm_peak", "pct_hbm_peak"):
@@ -943,6 +973,13 @@ def measure(torch, dev, wl, args, name, steps, warmup, cold_reps=0, probe=False,
             achieved=round(unique_call / dec_avg_s / 1e9, 2),
             frac=round(unique_call / dec_avg_s / 1e9 / HBM_PEAK_GBS, 4),
             bytes_per_launch=int(unique_call), logical_bytes_per_launch=run.algo_bytes)
+    b2b_us = result.get("pa_decode_us_back_to_back", result.get("pa_prefill_us_back_to_back"))
+    if b2b_us:                         # the same roofline on the back-to-back call time
+        rf = result["roofline"]
+        a = (pf["flops"] / (b2b_us * 1e-6) / 1e12 if rf["unit"] == "TFLOP/s"
+             else rf["bytes_per_launch"] / (b2b_us * 1e-6) / 1e9)
+        rf["achieved_back_to_back"] = round(a, 2)
+        rf["frac_back_to_back"] = round(a / rf["peak"], 4)
 
     if cold_reps > 0 and name in ("batch200", "batch10", "shared_prefix",
                                                 "vattention", "prefill_prompt",

@@ -339,10 +339,10 @@ __device__ __forceinline__ float wave_max(float x) {
 // group or has nothing to attend to; for a member of a group cut across
 // ranges, combine its partials (weights exp2(m_r - M)); otherwise nothing
 // (the decode kernel wrote the row).  A group can span many ranges, so the
-// pieces' (m, l) are read one per lane, at once, and the weighted sums of
-// eight pieces are loaded before they are added; a piece whose m is -inf
-// (no live token of the member in that range) has no weighted sums and is
-// left out by a select, so no stale value is ever multiplied.
+// pieces' (m, l) are read one per lane, at once; a piece whose m is -inf (no
+// live token of the member in that range) has no weighted sums and is left
+// out, and the weighted sums of the others are loaded eight at a time before
+// they are added.
 template <int D>
 __global__ __launch_bounds__(256) void pa_decode_grouped_merge_kernel(GroupArgs a) {
   constexpr int kPer = D / kWave;
@@ -395,14 +395,22 @@ __global__ __launch_bounds__(256) void pa_decode_grouped_merge_kernel(GroupArgs 
         den = fmaf(w, a.ws_ml[pc * 2 + 1], den);
       }
     }
-    const int cnt = min(kWave, r1 - base + 1);
-    for (int j0 = 0; j0 < cnt; j0 += kUnroll) {
+    // the pieces of this round that have weighted sums, in range order:
+    // lane j of the round is piece base + j; taken kUnroll at a time, their
+    // loads issued before they are added (a slot past the last one repeats
+    // it with weight 0)
+    uint64_t live = __builtin_amdgcn_ballot_w64(w != 0.0f);
+    while (live) {                     // uniform
       float acc_j[kUnroll][kPer];
       float w_j[kUnroll];
+      int last = 0;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int j = min(j0 + u, cnt - 1);
-        w_j[u] = j0 + u < cnt ? __shfl(w, j, kWave) : 0.0f;
+        const bool any = live != 0;
+        const int j = any ? __builtin_ctzll(live) : last;
+        live = any ? live & (live - 1) : live;
+        last = j;
+        w_j[u] = any ? __shfl(w, j, kWave) : 0.0f;
         const float* src = a.ws_acc + piece(base + j) * D + lane * kPer;
 #pragma unroll
         for (int e = 0; e < kPer; ++e) acc_j[u][e] = src[e];
