@@ -139,9 +139,22 @@ void pa_prefill_kernel(PrefillArgs a) {
   constexpr int R = 4;                                  // register ring: two pairs of tiles
   constexpr int kSlots = 3;                             // LDS pair slots
   static_assert(kUnits >= 1 && kLoaders % kWave == 0, "tile split; whole loading waves");
+  // Without the append, tiles go from HBM straight into LDS (no register
+  // ring); with it, through registers, since the item that owns an all-new
+  // block also writes it to the pools.
+  constexpr bool kDma = !kAppend;
+  static_assert(!kDma || kLoaders == kThreads, "every thread copies a share of each pair");
   extern __shared__ int smem[];
   __shared__ int s_wave[kPrefillWaves];
-  __shared__ u4v s_kv[2 * kSlots][2 * kTileUnits];     // tile stage: K tile, then V tile
+  // register-ring staging: three pair slots, each its K tile then V tile
+  __shared__ u4v s_kv[kDma ? 1 : 2 * kSlots][kDma ? 1 : 2 * kTileUnits];
+  // direct staging: four pair slots as four arrays, so that the compiler
+  // tells them apart when it places waits before LDS reads (a read of one
+  // slot does not wait for copies still landing in another)
+  __shared__ u4v s_d0[kDma ? 2 : 1][kDma ? 2 * kTileUnits : 1];
+  __shared__ u4v s_d1[kDma ? 2 : 1][kDma ? 2 * kTileUnits : 1];
+  __shared__ u4v s_d2[kDma ? 2 : 1][kDma ? 2 * kTileUnits : 1];
+  __shared__ u4v s_d3[kDma ? 2 : 1][kDma ? 2 * kTileUnits : 1];
   int* s_group = smem;                                  // B + 1
   int* s_ids = smem + a.B + 1;                          // block ids of the sequence
 
@@ -324,11 +337,11 @@ void pa_prefill_kernel(PrefillArgs a) {
 
       // Score products of the pair in pair slot sl (tiles 2 sl, 2 sl + 1):
       // S^T (32 tokens x 32 queries), register r = token 8*(r/4) + 4*hf + r%4.
-      auto scores = [&](int sl) {
+      auto scores = [&](const u4v* blk_a, const u4v* blk_b) {
         f16x16 sc;
   #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
-        const u4v* kt = s_kv[2 * sl + col / 16];
+        const u4v* kt = col < 16 ? blk_a : blk_b;
         u4v kr[kQK];                                      // A operands: token col of the pair
   #pragma unroll
         for (int i = 0; i < kQK; ++i) kr[i] = kt[k_unit + 2 * i * kBlockTokens];
@@ -383,7 +396,7 @@ void pa_prefill_kernel(PrefillArgs a) {
       // Second part: the fp16 weights (exp2(s |scale log2 e| - mref); a
       // masked score gives exp2(-inf) = 0), their running sum, and the value
       // products of the pair in pair slot sl.
-      auto weights_pv = [&](const f16x16& sc, float mref, int sl) {
+      auto weights_pv = [&](const f16x16& sc, float mref, const u4v* blk_a, const u4v* blk_b) {
         h8v pb[2];
   #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -402,7 +415,7 @@ void pa_prefill_kernel(PrefillArgs a) {
         for (int s = 0; s < kSl; ++s) {
   #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            const _Float16* vt = reinterpret_cast<const _Float16*>(&s_kv[2 * sl + kk][kTileUnits]);
+            const _Float16* vt = reinterpret_cast<const _Float16*>((kk ? blk_b : blk_a) + kTileUnits);
             const int off = s * 4 * kBlockTokens * 8;       // 4 dim groups per slice
             const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s4v*)(vt + off + tr_lo));
@@ -426,6 +439,7 @@ void pa_prefill_kernel(PrefillArgs a) {
       // every wave finished before the barrier of iteration p - 1.  Pairs past
       // the last block see valid = 0 (exact no-ops), so the loop runs whole
       // rounds of two pairs with no exit in its body.
+      if constexpr (!kDma) {
       u4v ring[R][kUnits];
       size_t ring_o[R];                                   // pool offsets of the ring's blocks
   #pragma unroll
@@ -438,7 +452,7 @@ void pa_prefill_kernel(PrefillArgs a) {
       // The two halves of a round alternate the score registers (sc_a holds
       // pair p's scores on entry), so no copy joins them.
       f16x16 sc_a = {}, sc_b = {};
-      if (wave_rows) sc_a = scores(0);
+      if (wave_rows) sc_a = scores(s_kv[0], s_kv[1]);
       const int npairs = (nblk + 1) / 2;
       int sl = 0;                                         // pair slot of pair p
       auto half = [&](int p, int u, f16x16& cur, f16x16& next) {
@@ -452,14 +466,91 @@ void pa_prefill_kernel(PrefillArgs a) {
         __syncthreads();
         if (wave_rows) {                                  // uniform per wave
           const float mref = prep(cur, p + u);
-          next = scores(sn);
-          weights_pv(cur, mref, sl);
+          next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
+          weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
         }
         sl = sn;
       };
       for (int p = 0; p < npairs; p += 2) {
         half(p, 0, sc_a, sc_b);
         half(p, 1, sc_b, sc_a);
+      }
+      } else {
+      // Direct staging.  Pair q goes from HBM (or L2) straight into slot q % 4
+      // (buffer_load ... lds: lane l's 16 bytes land at the slot position
+      // the wave's base names + 16 l, a load past the buffer range writes
+      // zeros).  Iteration i meets the barrier once this wave's copies of
+      // pair i + 1 are complete (those of pair i + 2 stay in flight), so
+      // after it every wave's are, and every wave has finished iteration
+      // i - 1: slot (i + 3) % 4, last read there, takes pair i + 3, two
+      // iterations ahead of its use.  The loop runs whole rounds of four
+      // pairs, so each slot is a fixed array in the unrolled body.
+      // (The barrier is written out: __syncthreads would also wait for the
+      // copies still in flight.)  Waits and barriers are fixed per iteration,
+      // so every wave takes the same path through them.
+      auto dma = [&](int q, u4v (*slot)[2 * kTileUnits]) {
+  #pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int j = 2 * q + hb;
+          const int jj = min(j, nblk - 1);
+          const uint32_t bytes = j < nblk ? kTile : 0u;
+          const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
+  #pragma unroll
+          for (int k = 0; k < kUnits; ++k) {
+            // this wave's 64 consecutive slot positions of copy k: K units
+            // p0 .. p0+63, or V positions p0 .. p0+63, which hold V units
+            // v_slot(p0 + lane) (the swizzle is its own inverse)
+            const int wbase = wave * kWave + kLoaders * k;   // uniform
+            const bool isv = wbase >= kTileUnits;             // uniform
+            const int p0 = isv ? wbase - kTileUnits : wbase;
+            const int src = isv ? v_slot(p0 + lane) : p0 + lane;
+            // V tokens past the context of the last block load as zeros
+            const bool zero = isv && j == nblk - 1 && src % kBlockTokens >= v_last;
+            const uint32_t off = zero ? 0x7FFFFFF0u : (uint32_t)src * 16u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                make_rsrc((isv ? vbase : kbase) + o, bytes),
+                (__attribute__((address_space(3))) void*)&slot[hb][(isv ? kTileUnits : 0) + p0],
+                16, off, 0, 0, 0);
+          }
+        }
+      };
+      auto sync_pair = [&]() {
+        if constexpr (2 * kUnits == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+      };
+      static_assert(2 * kUnits == 4 || 2 * kUnits == 2, "copies per pair");
+      dma(0, s_d0);
+      dma(1, s_d1);
+      dma(2, s_d2);
+      // pair 0 complete (pairs 1 and 2 in flight)
+      if constexpr (2 * kUnits == 4) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+      f16x16 sc_a = {}, sc_b = {};
+      if (wave_rows) sc_a = scores(s_d0[0], s_d0[1]);
+      const int npairs = (nblk + 1) / 2;
+      auto quarter = [&](int i, u4v (*cur_slot)[2 * kTileUnits],
+                         u4v (*next_slot)[2 * kTileUnits], u4v (*free_slot)[2 * kTileUnits],
+                         f16x16& cur, f16x16& next) {
+        sync_pair();
+        dma(i + 3, free_slot);
+        if (wave_rows) {                                  // uniform per wave
+          const float mref = prep(cur, i);
+          next = scores(next_slot[0], next_slot[1]);
+          weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
+        }
+      };
+      // (uniform exits after the last pair: the copies still in flight for
+      // pairs past the end write zeros and are waited for at the item's
+      // closing barrier)
+      for (int p = 0; p < npairs; p += 4) {
+        quarter(p, s_d0, s_d1, s_d3, sc_a, sc_b);
+        if (p + 1 >= npairs) break;
+        quarter(p + 1, s_d1, s_d2, s_d0, sc_b, sc_a);
+        if (p + 2 >= npairs) break;
+        quarter(p + 2, s_d2, s_d3, s_d1, sc_a, sc_b);
+        if (p + 3 >= npairs) break;
+        quarter(p + 3, s_d3, s_d0, s_d2, sc_b, sc_a);
+      }
       }
 
     }
