@@ -331,10 +331,21 @@ size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,
  *         non-decreasing, query_start[B] <= num_query_rows; rows outside
  *         [0, num_query_rows) are skipped).
  * host:   sizes, scale, max_context_len (>= every context_lens[b]; contexts
- *         are clamped to it), block_size 16, flags 0 (reserved).  The block
- *         ids of one sequence are staged in LDS: (B + 1 + max_context_len /
- *         16) * 4 bytes must not exceed 32 KiB.  No workspace.
+ *         are clamped to it), block_size 16, flags 0 or
+ *         PKV_PREFILL_HEADS_PER_ITEM(k).  The block ids of one sequence are
+ *         staged in LDS: (B + 1 + max_context_len / 16) * 4 bytes must not
+ *         exceed 32 KiB.  No workspace.
+ *
+ * Work decomposition: a workgroup takes 128 query rows of one sequence for
+ * k heads at a time (k = 1, 2, 4 or 8), and streams the sequence's blocks
+ * once per head, straight from one head into the next.  By default k is
+ * chosen from the sizes (the largest that keeps about four such items per
+ * resident workgroup); PKV_PREFILL_HEADS_PER_ITEM(k) fixes it.  The outputs
+ * are the same bit for bit for every k.
  */
+#define PKV_PREFILL_HEADS_PER_ITEM(k)                                            \
+  ((k) == 1 ? 1u << 8 : (k) == 2 ? 2u << 8 : (k) == 4 ? 3u << 8 : (k) == 8 ? 4u << 8 : 0xffu << 8)
+
 int pkv_pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                    const int32_t* block_tables, int32_t max_blocks_per_seq,
                    const int32_t* context_lens, int32_t max_context_len,

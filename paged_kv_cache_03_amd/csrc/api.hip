@@ -494,7 +494,9 @@ int prefill_call(const void* q, const void* k_new, const void* v_new, const void
                  int32_t D, int32_t block_size, int32_t num_blocks, float scale, void* out,
                  uint32_t flags, void* stream, bool append) {
   if (block_size != kBlockTokens) return PKV_ERR_UNSUPPORTED;
-  if (flags != 0) return PKV_ERR_BAD_SHAPE;
+  // flags: 0, or bits 8..15 = 1 + log2(heads per item), at most 8 heads
+  const uint32_t hcode = (flags >> 8) & 0xffu;
+  if ((flags & ~0xff00u) != 0 || hcode > 4) return PKV_ERR_BAD_SHAPE;
   if (!decode_shape_ok(B, H, D, max_context_len) || num_query_rows < 0 ||
       (long long)num_query_rows * H * D * 2 >= (1LL << 32))
     return PKV_ERR_BAD_SHAPE;
@@ -532,17 +534,31 @@ int prefill_call(const void* q, const void* k_new, const void* v_new, const void
   a.num_blocks = num_blocks;
   a.k_new = append ? static_cast<const _Float16*>(k_new) : nullptr;
   a.v_new = append ? static_cast<const _Float16*>(v_new) : nullptr;
-  // the items run in a grid-stride loop over at most eight workgroups per
-  // resident slot: few enough that no workgroup is launched only to find no
-  // item, enough that the hardware's dispatch still balances items of
-  // unequal length; a multiple of 8, so item i stays on XCD i % 8
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return PKV_ERR_HIP;
-  const long long resident = (long long)cus * pkv::kPrefillSlotsPerCU * 8 / 8 * 8;
-  const int grid = (int)(bound < resident ? bound : (resident > 0 ? resident : bound));
+  const long long slots = (long long)cus * pkv::kPrefillSlotsPerCU;   // resident workgroups
+  // Heads per item: the largest power of two (up to kPrefillMaxHeadsPerItem)
+  // that leaves about kPrefillItemsPerSlot items per resident workgroup,
+  // with the query groups estimated halfway between their bounds
+  // (ceil(rows / R) and that plus B).
+  const long long groups_est = ceil_div(num_query_rows, pkv::kPrefillRows) + B / 2;
+  int hpi = 1;
+  while (2 * hpi <= H && 2 * hpi <= pkv::kPrefillMaxHeadsPerItem &&
+         groups_est * ceil_div(H, 2 * hpi) >= pkv::kPrefillItemsPerSlot * slots)
+    hpi *= 2;
+  if (hcode != 0) hpi = 1 << (hcode - 1);
+  if (hpi > H) hpi = H;
+  a.heads_per_item = hpi;
+  // The items run in a grid-stride loop over at most eight workgroups per
+  // resident slot: few enough that no workgroup is launched only to find no
+  // item, enough that the hardware's dispatch still balances items of
+  // unequal length; a multiple of 8, so item i stays on XCD i % 8.
+  const long long items_bound = bound / H * ceil_div(H, hpi);
+  const long long grid_cap = slots * 8;
+  const int grid = (int)(items_bound < grid_cap ? items_bound : grid_cap);
   const hipError_t e =
       append ? pkv::launch_pa_prefill_append(a, D, grid, blocks_used, static_cast<hipStream_t>(stream))
              : pkv::launch_pa_prefill(a, D, grid, blocks_used, static_cast<hipStream_t>(stream));

@@ -98,6 +98,7 @@ struct FlatArgs {
   // in the pools before that position is read.
   const _Float16* k_new;
   const _Float16* v_new;
+  int heads_per_item;           // heads of one query group per work item (>= 1)
 };
 
 // Grouped decode (pa_decode_grouped.hip): groups of up to kGroupMaxMembers
@@ -139,7 +140,8 @@ struct GroupArgs {
   bool keep_cached;
 };
 
-// Prefill (pa_prefill.hip): one workgroup per (128 query rows, head).
+// Prefill (pa_prefill.hip): work items of (128 query rows, a few heads),
+// one workgroup at a time.
 #ifndef PKV_PREFILL_WAVES
 #define PKV_PREFILL_WAVES 4
 #endif
@@ -147,6 +149,10 @@ constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, 32 qu
 constexpr int kPrefillRows = 32 * kPrefillWaves;
 constexpr int kPrefillMaxLdsBytes = 32 * 1024;
 constexpr int kPrefillSlotsPerCU = 2;      // resident workgroups per CU (two waves per SIMD)
+// heads per item: as many as keep about this many items per resident
+// workgroup (enough for the dispatch to balance items of unequal length)
+constexpr int kPrefillItemsPerSlot = 8;
+constexpr int kPrefillMaxHeadsPerItem = 8;
 
 struct PrefillArgs {
   const _Float16* q;            // [num_rows][H][D]
@@ -166,6 +172,7 @@ struct PrefillArgs {
   // tokens' keys and values, [num_rows][H][D] like q; null otherwise
   const _Float16* k_new;
   const _Float16* v_new;
+  int heads_per_item;           // heads of one query group per work item (>= 1)
 };
 
 struct AppendArgs {

@@ -33,10 +33,16 @@
 //    4h .. 4h+3 and 8+4h .. 8+4h+3).
 // Blocks past a row's position are exact no-ops for it (causal mask per
 // element), so a row's result does not depend on the rows it shares a
-// workgroup with.  Workgroups take (query group, head) items in a
-// grid-stride loop; item i serves head i % H, and with a grid that is a
-// multiple of 8 it runs on XCD i % 8 (one XCD per head when H is a multiple
-// of 8).  Within a sequence the groups that reach furthest come first.
+// workgroup with.  Workgroups take (query group, head group) items in a
+// grid-stride loop: an item covers a few consecutive heads of one query
+// group, and its tile pipeline runs straight through them (the next head's
+// queries are loaded while the last pair of the current one is in flight,
+// a finished head's rows are written at the next step), so the set-up of an
+// item and the fill of its pipeline are paid once per head group.  Item i
+// serves head group i % G (G head groups), and with a grid that is a
+// multiple of 8 it runs on XCD i % 8 (one XCD per head group when G is a
+// multiple of 8).  Within a sequence the groups that reach furthest come
+// first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,6 +57,13 @@ namespace {
 using namespace dev;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// s_waitcnt operand for "at most n vector memory operations outstanding"
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima, so they do not wait)
+constexpr unsigned waitcnt_vm(unsigned n) {
+  return (n & 0xfu) | ((n >> 4) << 14) | (0x7u << 4) | (0xfu << 8);
+}
 
 // LDS slot of V unit u = g * 16 + token (8 dims of dim group g of one
 // token): the token index is XOR-ed with 4 * (g % 4), so that the 16 lanes
@@ -123,7 +136,7 @@ __device__ __forceinline__ int seq_of_group(const int* s_group, int B, int t) {
 // item whose query rows hold a block's first token writes that block to
 // the pools as it stages it (a store with an empty range for the other
 // tiles), so the load ring keeps its fixed shape.
-template <int D, bool kAppend>
+template <int D, bool kAppend, bool kMulti>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pa_prefill_kernel(PrefillArgs a) {
   typedef float f16x16 __attribute__((ext_vector_type(16)));
@@ -165,13 +178,19 @@ void pa_prefill_kernel(PrefillArgs a) {
   const int hf = lane / 32;                             // k-slot half of this lane
 
   group_prefix(a, s_group, s_wave);
-  // Items (query group, head), longest-reaching groups first, in a
+  // Items (query group, head group), longest-reaching groups first, in a
   // grid-stride loop: the prefix above is computed once per workgroup for
-  // its few items, and no workgroup is launched only to find none.
-  const int items = s_group[a.B] * a.H;
+  // its few items, and no workgroup is launched only to find none.  An item
+  // covers heads h0 .. h0 + nh - 1 of its query group: the sequence's
+  // parameters and block ids are set up once, and the tile pipeline runs on
+  // across the head boundaries as over one sequence of nh * npairs pairs.
+  const int hpi = a.heads_per_item;
+  const int hgroups = (a.H + hpi - 1) / hpi;
+  const int items = s_group[a.B] * hgroups;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int gt = item / a.H;
-    const int h = item % a.H;
+    const int gt = item / hgroups;
+    const int h0 = (item - gt * hgroups) * hpi;
+    const int nh = kMulti ? min(hpi, a.H - h0) : 1;
     const int b = seq_of_group(s_group, a.B, gt);
     const int n = rows_of(a, b);
     const int kq = groups_of(a, b) - 1 - (gt - s_group[b]);   // furthest-reaching group first
@@ -203,24 +222,31 @@ void pa_prefill_kernel(PrefillArgs a) {
     const bool row_ok = wrow < grows && qrow >= 0 && qrow < a.num_rows;
     const int p_q = p_group + wrow;
     const rsrc_t qr = make_rsrc(a.q, (uint32_t)((size_t)a.num_rows * a.H * D * 2));
-    const uint32_t qoff = row_ok ? (uint32_t)((((size_t)qrow * a.H + h) * D + 8 * hf) * 2)
-                                 : 0xFFFFFFF0u;           // past the resource: reads 0
+    const uint32_t qrow_off = (uint32_t)(((size_t)qrow * a.H * D + 8 * hf) * 2);
     h8v qb[kQK];                                          // B operands: dims 16i + 8hf ..
+    // the queries of head h (no row: past the resource, reads 0)
+    auto load_q = [&](int h) {
+      const uint32_t off = row_ok ? qrow_off + (uint32_t)(h * D * 2) : 0xFFFFFFF0u;
   #pragma unroll
-    for (int i = 0; i < kQK; ++i)
-      qb[i] = as_h8(__builtin_amdgcn_raw_buffer_load_b128(qr, qoff + (row_ok ? i * 32 : 0), 0, 0));
-    // keep the query loads ahead of the ring's first tiles (every step reads them)
-    __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < kQK; ++i)
+        qb[i] = as_h8(__builtin_amdgcn_raw_buffer_load_b128(qr, off + (row_ok ? i * 32 : 0), 0, 0));
+    };
     // The scores are taken as (sign(scale) q) . k (an exact negation), so that
     // their maximum is the maximum of the scaled scores; weights are then
     // exp2(s * |scale log2 e| - m) with one fused multiply-add.
     // (a zero scale is taken as the smallest normal float: the weights are
     // then exactly 1, and a masked score's -inf times it stays -inf)
     const float sabs = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
-    if (a.scale_log2 < 0.0f) {
+    auto sign_q = [&]() {
+      if (a.scale_log2 < 0.0f) {
   #pragma unroll
-      for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
-    }
+        for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
+      }
+    };
+    load_q(h0);
+    // keep the query loads ahead of the ring's first tiles (every step reads them)
+    __builtin_amdgcn_sched_barrier(0);
+    sign_q();
     const int p_wave = p_group + 32 * wave;               // position of the wave's first row
 
     float m = kNegInf, l = 0.0f;        // reference maximum (scaled, log2); sum over this lane's tokens
@@ -230,8 +256,36 @@ void pa_prefill_kernel(PrefillArgs a) {
   #pragma unroll
       for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
 
-    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h * kTile;
-    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h * kTile;
+    // Output rows of head h from the sums, which then restart for the next
+    // head.  Rows at a negative position (more queries than cached tokens)
+    // are zero; lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row.
+    auto finish = [&](int h) {
+      auto sw = __builtin_amdgcn_permlane32_swap(as_u32(l), as_u32(l), false, false);
+      const float lt = as_f32(sw[0]) + as_f32(sw[1]);
+      if (row_ok) {
+        const float inv = p_q >= 0 && lt > 0.0f ? 1.0f / lt : 0.0f;
+        _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * hf;
+  #pragma unroll
+        for (int s = 0; s < kSl; ++s)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            h4v o;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][4 * q + r] * inv);
+            *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
+          }
+      }
+      m = kNegInf;
+      l = 0.0f;
+  #pragma unroll
+      for (int s = 0; s < kSl; ++s)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+    };
+
+    // head h0 + hl of block id: pool offset id * block_stride + hl * kTile
+    const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (size_t)h0 * kTile;
+    const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (size_t)h0 * kTile;
     const size_t block_stride = (size_t)a.H * kTile;
     // The tile pair is 2 * kTileUnits 16-byte units; the first kLoaders
     // threads load them, unit u = tid + kLoaders * k (K for u < kTileUnits,
@@ -253,19 +307,32 @@ void pa_prefill_kernel(PrefillArgs a) {
     const int row_r = a.query_start[b] - bnd + t_r;
     const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
     const uint32_t rows_total = (uint32_t)a.num_rows * row_bytes;
-    // byte offset of token t_r of block 0 (modulo 2^32: row_r may be
-    // negative, the rows of the tokens that exist are not)
-    const uint32_t row_base = (uint32_t)row_r * row_bytes + (uint32_t)((h * D + 8 * g_r) * 2);
+    // byte offset of token t_r of block 0, head h0 (modulo 2^32: row_r may
+    // be negative, the rows of the tokens that exist are not)
+    const uint32_t row_base = (uint32_t)row_r * row_bytes + (uint32_t)((h0 * D + 8 * g_r) * 2);
     // Token t_r of block j exists if it lies inside the context; tiles at or
     // past nblk read as zeros.  With query_start inside [0, num_rows] its row
     // is one of the sequence's; the buffer bounds keep any other row inside
     // the caller's rows.
-    auto row_off = [&](int j) {
+    auto row_off = [&](int j, int hl) {
       return j < nblk && t_r < ctx - kBlockTokens * j
-                 ? row_base + (uint32_t)j * (uint32_t)kBlockTokens * row_bytes
+                 ? row_base + (uint32_t)(hl * D * 2) + (uint32_t)j * (uint32_t)kBlockTokens * row_bytes
                  : 0xFFFFFFF0u;
     };
     if (nblk > 0) {
+      const int npairs = (nblk + 1) / 2;                  // pairs of blocks per head
+      const int nv = nh * npairs;                         // pairs over the item's heads
+      // (head, pair) cursors run through the item's pairs in order
+      auto advance = [&](int& hl, int& pp) {
+        if constexpr (kMulti) {
+          if (++pp == npairs) {
+            pp = 0;
+            ++hl;
+          }
+        } else {
+          ++pp;                                           // one head: past npairs reads zeros
+        }
+      };
       // V token slots past the context must hold zeros (their weight is 0,
       // and 0 times stale data could be NaN).  Only the last block can be
       // partial: there the lanes of those tokens read past the resource,
@@ -273,16 +340,18 @@ void pa_prefill_kernel(PrefillArgs a) {
       const int v_last = ctx - (nblk - 1) * kBlockTokens;   // valid tokens of the last block
       const uint32_t v_off_last =
           (int)((tid % kTileUnits) % kBlockTokens) < v_last ? unit_off : 0x7FFFFFF0u;
-      // o returns the block's pool offset; with the append its bit 0 is set
+      // Block j of head h0 + hl (hl >= nh: past the item, reads zeros).  o
+      // returns the tile's pool offset; with the append its bit 0 is set
       // when the table entry lies outside the pool (offsets are multiples of
-      // a tile, so bit 0 is free).
-      auto fetch = [&](u4v (&r)[kUnits], size_t& o, int j) {
+      // 16, so bit 0 is free).
+      auto fetch = [&](u4v (&r)[kUnits], size_t& o, int j, int hl) {
+        const bool live = !kMulti || hl < nh;             // uniform
         const int jj = min(j, nblk - 1);
-        const uint32_t bytes = j < nblk && loader ? kTile : 0u;
+        const uint32_t bytes = live && j < nblk && loader ? kTile : 0u;
         const int raw = __builtin_amdgcn_readfirstlane(s_ids[jj]);
-        o = (size_t)(raw & 0x7fffffff) * block_stride;
+        o = (size_t)(raw & 0x7fffffff) * block_stride + (size_t)hl * kTile;
         const bool rows = kAppend && j >= jn;             // uniform
-        const uint32_t roff = kAppend ? row_off(j) : 0u;
+        const uint32_t roff = kAppend ? row_off(live ? j : nblk, hl) : 0u;
   #pragma unroll
         for (int k = 0; k < kUnits; ++k) {
           const uint32_t off = unit_is_v(k) && j == nblk - 1 ? v_off_last : unit_off;
@@ -298,21 +367,21 @@ void pa_prefill_kernel(PrefillArgs a) {
         }
         if constexpr (kAppend) o |= (size_t)(raw < 0);
       };
-      // Stage block j's tiles (pool offset o) into pair slot half st.  With
-      // the append, a tile read from the rows also goes to its pool
-      // block when this item owns the block (its rows hold the block's first
-      // token): the store is issued for every tile, with an empty range when
-      // the item does not own it, so the ring's wait counts stay fixed.
-      auto stage = [&](const u4v (&r)[kUnits], int st, int j, size_t o) {
+      // Stage block j of head h0 + hl (pool offset o) into pair slot half
+      // st.  With the append, a tile read from the rows also goes to its
+      // pool block when this item owns the block (its rows hold the block's
+      // first token): the store is issued for every tile, with an empty
+      // range when the item does not own it, so the ring's wait counts stay
+      // fixed.
+      auto stage = [&](const u4v (&r)[kUnits], int st, int j, int hl, size_t o) {
         if (!loader) return;                              // uniform per wave
         const int u = tid % kTileUnits;
-        const bool rows = kAppend && j >= jn;             // uniform
   #pragma unroll
         for (int k = 0; k < kUnits; ++k)
           s_kv[st][unit_is_v(k) ? kTileUnits + v_slot(u) : u] = r[k];
         if constexpr (kAppend) {
           // a block whose table entry lies outside the pool is not written
-          const bool own = rows && j < nblk && !(o & 1) &&
+          const bool own = j >= jn && hl < nh && j < nblk && !(o & 1) &&
                            (kBlockTokens * j - bnd) / kPrefillRows == kq;
           const size_t ob = o & ~(size_t)1;
           const uint32_t woff = t_r < ctx - kBlockTokens * j ? (uint32_t)u_r * 16u : 0xFFFFFFF0u;
@@ -335,7 +404,7 @@ void pa_prefill_kernel(PrefillArgs a) {
       // this lane's K row: token col of the pair (tile col / 16), dims 16i + 8hf ..
       const int k_unit = hf * kBlockTokens + col % 16;    // + 2i * 16 per MFMA
 
-      // Score products of the pair in pair slot sl (tiles 2 sl, 2 sl + 1):
+      // Score products of the pair whose tiles are at blk_a and blk_b:
       // S^T (32 tokens x 32 queries), register r = token 8*(r/4) + 4*hf + r%4.
       auto scores = [&](const u4v* blk_a, const u4v* blk_b) {
         f16x16 sc;
@@ -351,11 +420,11 @@ void pa_prefill_kernel(PrefillArgs a) {
         return sc;
       };
 
-      // Softmax of pair pp (blocks 2 pp, 2 pp + 1), first part: mask the
-      // scores (masked ones become -inf), raise the reference maximum if
-      // needed (rescaling the sums), return the reference for the weights.
-      // All the branches of the step are here, so that the rest of the step
-      // and the next pair's score products share one basic block.
+      // Softmax of pair pp of a head (blocks 2 pp, 2 pp + 1), first part:
+      // mask the scores (masked ones become -inf), raise the reference
+      // maximum if needed (rescaling the sums), return the reference for the
+      // weights.  All the branches of the step are here, so that the rest of
+      // the step and the next pair's score products share one basic block.
       auto prep = [&](f16x16& sc, int pp) {
         const int j = 2 * pp;
         const int t0 = j * kBlockTokens;
@@ -395,7 +464,7 @@ void pa_prefill_kernel(PrefillArgs a) {
 
       // Second part: the fp16 weights (exp2(s |scale log2 e| - mref); a
       // masked score gives exp2(-inf) = 0), their running sum, and the value
-      // products of the pair in pair slot sl.
+      // products of the pair whose tiles are at blk_a and blk_b.
       auto weights_pv = [&](const f16x16& sc, float mref, const u4v* blk_a, const u4v* blk_b) {
         h8v pb[2];
   #pragma unroll
@@ -428,6 +497,17 @@ void pa_prefill_kernel(PrefillArgs a) {
         }
       };
 
+      // Head boundaries inside the pipeline.  With the computed pair at
+      // (head ch, pair cp) of the item:
+      //  * when cp == 0 and ch > 0, head ch - 1 is complete: its rows are
+      //    written and the sums restart, before this pair's softmax;
+      //  * the queries of head ch + 1 are loaded into qb right after the
+      //    score products of head ch's last pair were issued (one step
+      //    before that pair's softmax), so they are in registers by the time
+      //    the first pair of head ch + 1 needs them.
+      // next_is_last: the pair after (ch, cp) is the last pair of its head.
+      auto next_is_last = [&](int cp) { return npairs == 1 || cp + 2 == npairs; };
+
       // Software pipeline over pairs of blocks.  Pair p lives in LDS pair
       // slot p % 3; its two tiles come through a register ring of four tiles
       // (two pairs), fetched two pairs before they are staged.  Iteration p
@@ -436,44 +516,72 @@ void pa_prefill_kernel(PrefillArgs a) {
       // the score products of pair p + 1 in one basic block with the weights
       // and value products of pair p, which do not depend on them.
       // The slot staged in iteration p was last read in iteration p - 2, which
-      // every wave finished before the barrier of iteration p - 1.  Pairs past
-      // the last block see valid = 0 (exact no-ops), so the loop runs whole
-      // rounds of two pairs with no exit in its body.
+      // every wave finished before the barrier of iteration p - 1.  The loop
+      // runs whole rounds of two pairs with no exit in its body; a pair past
+      // the item's last one is all masked (an exact no-op).
       if constexpr (!kDma) {
       u4v ring[R][kUnits];
-      size_t ring_o[R];                                   // pool offsets of the ring's blocks
+      size_t ring_o[R];                                   // pool offsets of the ring's tiles
+      int ring_j[R], ring_h[R];                           // (block, head) of the ring's tiles
+      int fh = 0, fp = 0;                                 // the pair fetched next
+      // ring tile r takes block hb of pair (fh, fp); the pair advances after hb = 1
+      auto fetch_tile = [&](int r, int hb) {
+        ring_j[r] = 2 * fp + hb;
+        ring_h[r] = fh;
+        fetch(ring[r], ring_o[r], 2 * fp + hb, fh);
+        if (hb) advance(fh, fp);
+      };
+      auto stage_tile = [&](int r, int st) { stage(ring[r], st, ring_j[r], ring_h[r], ring_o[r]); };
   #pragma unroll
-      for (int r = 0; r < R; ++r) fetch(ring[r], ring_o[r], r);
-      stage(ring[0], 0, 0, ring_o[0]);
-      stage(ring[1], 1, 1, ring_o[1]);
-      fetch(ring[0], ring_o[0], 4);
-      fetch(ring[1], ring_o[1], 5);
+      for (int r = 0; r < R; ++r) fetch_tile(r, r % 2);
+      stage_tile(0, 0);
+      stage_tile(1, 1);
+      fetch_tile(0, 0);
+      fetch_tile(1, 1);
       __syncthreads();
       // The two halves of a round alternate the score registers (sc_a holds
       // pair p's scores on entry), so no copy joins them.
       f16x16 sc_a = {}, sc_b = {};
-      if (wave_rows) sc_a = scores(s_kv[0], s_kv[1]);
-      const int npairs = (nblk + 1) / 2;
-      int sl = 0;                                         // pair slot of pair p
-      auto half = [&](int p, int u, f16x16& cur, f16x16& next) {
-        const int pn = p + u + 1;                         // the pair staged now
+      if (wave_rows) {
+        sc_a = scores(s_kv[0], s_kv[1]);
+        if constexpr (kMulti) {
+          if (npairs == 1 && nh > 1) load_q(h0 + 1);
+        }
+      }
+      int ch = 0, cp = 0;                                 // the pair computed now
+      int sl = 0;                                         // its pair slot
+      auto half = [&](int u, f16x16& cur, f16x16& next) {
         const int sn = sl == kSlots - 1 ? 0 : sl + 1;
-        const int ra = (2 * (u + 1)) % R;                 // its ring tiles
-        stage(ring[ra], 2 * sn, 2 * pn, ring_o[ra]);
-        fetch(ring[ra], ring_o[ra], 2 * pn + R);
-        stage(ring[ra + 1], 2 * sn + 1, 2 * pn + 1, ring_o[ra + 1]);
-        fetch(ring[ra + 1], ring_o[ra + 1], 2 * pn + 1 + R);
+        const int ra = (2 * (u + 1)) % R;                 // ring tiles of the pair staged now
+        if constexpr (kMulti) {
+          if (cp == 0 && ch > 0 && ch < nh && wave_rows) finish(h0 + ch - 1);
+        }
+        stage_tile(ra, 2 * sn);
+        fetch_tile(ra, 0);
+        stage_tile(ra + 1, 2 * sn + 1);
+        fetch_tile(ra + 1, 1);
         __syncthreads();
         if (wave_rows) {                                  // uniform per wave
-          const float mref = prep(cur, p + u);
-          next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
-          weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
+          if constexpr (kMulti) {
+            const bool cur_last = cp == npairs - 1;
+            const float mref = prep(cur, ch < nh ? cp : npairs);
+            if (cur_last && ch + 1 < nh) sign_q();
+            next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
+            if (next_is_last(cp) && (cur_last ? ch + 1 : ch) + 1 < nh)
+              load_q(h0 + (cur_last ? ch + 1 : ch) + 1);
+            weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
+          } else {
+            const float mref = prep(cur, cp);
+            next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
+            weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
+          }
         }
+        advance(ch, cp);
         sl = sn;
       };
-      for (int p = 0; p < npairs; p += 2) {
-        half(p, 0, sc_a, sc_b);
-        half(p, 1, sc_b, sc_a);
+      for (int v = 0; v < nv; v += 2) {
+        half(0, sc_a, sc_b);
+        half(1, sc_b, sc_a);
       }
       } else {
       // Direct staging.  Pair q goes from HBM (or L2) straight into slot q % 4
@@ -484,17 +592,26 @@ void pa_prefill_kernel(PrefillArgs a) {
       // after it every wave's are, and every wave has finished iteration
       // i - 1: slot (i + 3) % 4, last read there, takes pair i + 3, two
       // iterations ahead of its use.  The loop runs whole rounds of four
-      // pairs, so each slot is a fixed array in the unrolled body.
-      // (The barrier is written out: __syncthreads would also wait for the
-      // copies still in flight.)  Waits and barriers are fixed per iteration,
-      // so every wave takes the same path through them.
-      auto dma = [&](int q, u4v (*slot)[2 * kTileUnits]) {
+      // pairs, so each slot is a fixed array in the unrolled body.  (The
+      // barrier is written out: __syncthreads would also wait for the copies
+      // still in flight.)  Each wave meets exactly one barrier per iteration.
+      //
+      // Over several heads, the copies of a step are issued after its score
+      // products and after the next head's query loads (when that step
+      // issues them), and the step ends waiting for all but its own copies
+      // (what the next barrier waits for anyway): so the query loads are
+      // complete by the next step, and the compiler, which cannot tell the
+      // steps that issue them, places no wait for them in the others.
+      int fh = 0, fp = 0;                                 // the pair copied next
+      auto dma = [&](u4v (*slot)[2 * kTileUnits]) {
+        const bool live = !kMulti || fh < nh;             // uniform
   #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const int j = 2 * q + hb;
+          const int j = 2 * fp + hb;
           const int jj = min(j, nblk - 1);
-          const uint32_t bytes = j < nblk ? kTile : 0u;
-          const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride;
+          const uint32_t bytes = live && j < nblk ? kTile : 0u;
+          const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride +
+                           (size_t)fh * kTile;
   #pragma unroll
           for (int k = 0; k < kUnits; ++k) {
             // this wave's 64 consecutive slot positions of copy k: K units
@@ -513,64 +630,74 @@ void pa_prefill_kernel(PrefillArgs a) {
                 16, off, 0, 0, 0);
           }
         }
-      };
-      auto sync_pair = [&]() {
-        if constexpr (2 * kUnits == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+        advance(fh, fp);
       };
       static_assert(2 * kUnits == 4 || 2 * kUnits == 2, "copies per pair");
-      dma(0, s_d0);
-      dma(1, s_d1);
-      dma(2, s_d2);
-      // pair 0 complete (pairs 1 and 2 in flight)
-      if constexpr (2 * kUnits == 4) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+      dma(s_d0);
+      dma(s_d1);
+      dma(s_d2);
+      // The first three pairs complete (issued together, they land close
+      // together; the compiler would place this wait before the first LDS
+      // read on its own, since it does not tell the copies issued here
+      // apart).
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      asm volatile("s_barrier" ::: "memory");
       f16x16 sc_a = {}, sc_b = {};
-      if (wave_rows) sc_a = scores(s_d0[0], s_d0[1]);
-      const int npairs = (nblk + 1) / 2;
-      auto quarter = [&](int i, u4v (*cur_slot)[2 * kTileUnits],
-                         u4v (*next_slot)[2 * kTileUnits], u4v (*free_slot)[2 * kTileUnits],
-                         f16x16& cur, f16x16& next) {
-        sync_pair();
-        dma(i + 3, free_slot);
-        if (wave_rows) {                                  // uniform per wave
-          const float mref = prep(cur, i);
-          next = scores(next_slot[0], next_slot[1]);
-          weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
+      if (wave_rows) {
+        sc_a = scores(s_d0[0], s_d0[1]);
+        if constexpr (kMulti) {
+          // one pair per head: the next head's queries now
+          if (npairs == 1 && nh > 1) {
+            load_q(h0 + 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          }
         }
+      }
+      int ch = 0, cp = 0;                                 // the pair computed now
+      auto quarter = [&](u4v (*cur_slot)[2 * kTileUnits], u4v (*next_slot)[2 * kTileUnits],
+                         u4v (*free_slot)[2 * kTileUnits], f16x16& cur, f16x16& next) {
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kUnits) : "memory");
+        if constexpr (!kMulti) {
+          dma(free_slot);
+          if (wave_rows) {                                // uniform per wave
+            const float mref = prep(cur, cp);
+            next = scores(next_slot[0], next_slot[1]);
+            weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
+          }
+        } else {
+          if (cp == 0 && ch > 0 && wave_rows) finish(h0 + ch - 1);
+          const bool cur_last = cp == npairs - 1;
+          const bool qnew = wave_rows && next_is_last(cp) && (cur_last ? ch + 1 : ch) + 1 < nh;
+          float mref = 0.0f;
+          if (wave_rows) {                                // uniform per wave
+            mref = prep(cur, cp);
+            if (cur_last && ch + 1 < nh) sign_q();
+            next = scores(next_slot[0], next_slot[1]);
+            if (qnew) load_q(h0 + (cur_last ? ch + 1 : ch) + 1);
+          }
+          dma(free_slot);
+          if (wave_rows) weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kUnits));
+        }
+        advance(ch, cp);
       };
       // (uniform exits after the last pair: the copies still in flight for
       // pairs past the end write zeros and are waited for at the item's
       // closing barrier)
-      for (int p = 0; p < npairs; p += 4) {
-        quarter(p, s_d0, s_d1, s_d3, sc_a, sc_b);
-        if (p + 1 >= npairs) break;
-        quarter(p + 1, s_d1, s_d2, s_d0, sc_b, sc_a);
-        if (p + 2 >= npairs) break;
-        quarter(p + 2, s_d2, s_d3, s_d1, sc_a, sc_b);
-        if (p + 3 >= npairs) break;
-        quarter(p + 3, s_d3, s_d0, s_d2, sc_b, sc_a);
+      for (int v = 0; v < nv; v += 4) {
+        quarter(s_d0, s_d1, s_d3, sc_a, sc_b);
+        if (v + 1 >= nv) break;
+        quarter(s_d1, s_d2, s_d0, sc_b, sc_a);
+        if (v + 2 >= nv) break;
+        quarter(s_d2, s_d3, s_d1, sc_a, sc_b);
+        if (v + 3 >= nv) break;
+        quarter(s_d3, s_d0, s_d2, sc_b, sc_a);
       }
       }
-
-    }
-
-    // rows at a negative position (more queries than cached tokens) are zero;
-    // lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row
-    auto sw = __builtin_amdgcn_permlane32_swap(as_u32(l), as_u32(l), false, false);
-    l = as_f32(sw[0]) + as_f32(sw[1]);
-    if (row_ok) {
-      const float inv = p_q >= 0 && l > 0.0f ? 1.0f / l : 0.0f;
-      _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * hf;
-  #pragma unroll
-      for (int s = 0; s < kSl; ++s)
-  #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          h4v o;
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][4 * q + r] * inv);
-          *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
-        }
+      finish(h0 + nh - 1);
+    } else {
+      // no token to attend: every head's rows are zero
+      for (int hl = 0; hl < nh; ++hl) finish(h0 + hl);
     }
 
     __syncthreads();                                    // LDS staging is reused by the next item
@@ -617,14 +744,34 @@ size_t prefill_lds_bytes(int B, int max_blocks_used) {
   return (size_t)(B + 1 + max_blocks_used) * sizeof(int);
 }
 
+namespace {
+
+template <bool kAppend>
+void launch_prefill_kernel(const PrefillArgs& a, int D, int grid, size_t lds, hipStream_t stream) {
+  const int threads = kWave * kPrefillWaves;
+  const bool multi = a.heads_per_item > 1;
+  if (D == 128) {
+    if (multi)
+      hipLaunchKernelGGL((pa_prefill_kernel<128, kAppend, true>), dim3(grid), dim3(threads), lds,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_kernel<128, kAppend, false>), dim3(grid), dim3(threads), lds,
+                         stream, a);
+  } else {
+    if (multi)
+      hipLaunchKernelGGL((pa_prefill_kernel<64, kAppend, true>), dim3(grid), dim3(threads), lds,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_kernel<64, kAppend, false>), dim3(grid), dim3(threads), lds,
+                         stream, a);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_pa_prefill(const PrefillArgs& a, int D, int grid, int max_blocks_used,
                              hipStream_t stream) {
-  const size_t lds = prefill_lds_bytes(a.B, max_blocks_used);
-  const int threads = kWave * kPrefillWaves;
-  if (D == 128)
-    hipLaunchKernelGGL((pa_prefill_kernel<128, false>), dim3(grid), dim3(threads), lds, stream, a);
-  else
-    hipLaunchKernelGGL((pa_prefill_kernel<64, false>), dim3(grid), dim3(threads), lds, stream, a);
+  launch_prefill_kernel<false>(a, D, grid, prefill_lds_bytes(a.B, max_blocks_used), stream);
   return hipGetLastError();
 }
 
@@ -636,12 +783,7 @@ hipError_t launch_pa_prefill_append(const PrefillArgs& a, int D, int grid, int m
     hipLaunchKernelGGL((prefill_boundary_append_kernel<64>), dim3(a.B), dim3(256), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = prefill_lds_bytes(a.B, max_blocks_used);
-  const int threads = kWave * kPrefillWaves;
-  if (D == 128)
-    hipLaunchKernelGGL((pa_prefill_kernel<128, true>), dim3(grid), dim3(threads), lds, stream, a);
-  else
-    hipLaunchKernelGGL((pa_prefill_kernel<64, true>), dim3(grid), dim3(threads), lds, stream, a);
+  launch_prefill_kernel<true>(a, D, grid, prefill_lds_bytes(a.B, max_blocks_used), stream);
   return hipGetLastError();
 }
 

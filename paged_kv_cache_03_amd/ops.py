@@ -249,29 +249,37 @@ def pa_decode_append_noalloc(q, k_new, v_new, k_pool, v_pool, block_tables, cont
 
 
 def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, out=None, *,
-               max_context_len=None):
+               max_context_len=None, heads_per_item=None):
     """Causal attention of each sequence's last n_b cached tokens (its rows
     query_start[b] .. query_start[b+1]-1 of q, [T][H][D] fp16) over its paged
     cache: row i of sequence b sits at position context_lens[b] - n_b + i.
     ``query_start`` is an int32 device tensor of B+1 entries; the other
-    arguments are as for ``pa_decode``."""
+    arguments are as for ``pa_decode``.  ``heads_per_item`` (1, 2, 4 or 8;
+    None: chosen from the sizes) sets how many heads of one 128-row query
+    group a workgroup takes at a time; the output does not depend on it."""
     return _prefill(q, None, None, k_pool, v_pool, block_tables, context_lens, query_start,
-                    scale, out, max_context_len)
+                    scale, out, max_context_len, heads_per_item)
 
 
 def pa_prefill_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_start,
-                      scale, out=None, *, max_context_len=None):
+                      scale, out=None, *, max_context_len=None, heads_per_item=None):
     """``pa_prefill`` with the append of the new tokens fused in: row r of
     k_new / v_new ([T][H][D] fp16, like q) is written to the slot of its
     position (through the block table) in both pools, and the queries attend
     as for ``pa_prefill``; ``context_lens`` counts the new tokens.  Pools and
     output equal ``kv_append`` followed by ``pa_prefill`` bit for bit."""
     return _prefill(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_start,
-                    scale, out, max_context_len)
+                    scale, out, max_context_len, heads_per_item)
+
+
+_HEADS_CODE = {None: 0, 1: 1, 2: 2, 4: 3, 8: 4}
 
 
 def _prefill(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_start, scale,
-             out, max_context_len):
+             out, max_context_len, heads_per_item):
+    if heads_per_item not in _HEADS_CODE:
+        raise ValueError("heads_per_item must be None, 1, 2, 4 or 8")
+    flags = _HEADS_CODE[heads_per_item] << 8
     lib = _lib.load_library()
     _need(q, "q", torch.float16, ndim=3)
     dev = q.device
@@ -301,7 +309,7 @@ def _prefill(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, query_
     if append and validate.debug_enabled():
         validate.check_prefill_append(block_tables, context_lens, query_start)
     tail = (_ptr(block_tables), block_tables.shape[1], _ptr(context_lens), max_context_len,
-            _ptr(query_start), T, B, H, D, BLOCK_TOKENS, NB, float(scale), _ptr(out), 0,
+            _ptr(query_start), T, B, H, D, BLOCK_TOKENS, NB, float(scale), _ptr(out), flags,
             _stream_handle(dev))
     with torch.cuda.device(dev):
         if append:

@@ -297,6 +297,13 @@ def test_prefill_rejects_bad_arguments(lib):
 
     assert call(bs=8) == _lib.ERR_UNSUPPORTED
     assert call(flags=1) == _lib.ERR_BAD_SHAPE
+    # heads per item: codes 1..4 (1, 2, 4, 8 heads) in bits 8..15; an
+    # accepted code passes the flag check (the null q then fails)
+    for code in (1, 2, 3, 4):
+        assert call(flags=code << 8, q=None) == _lib.ERR_NULL_PTR
+    assert call(flags=5 << 8) == _lib.ERR_BAD_SHAPE
+    assert call(flags=(1 << 8) | 1) == _lib.ERR_BAD_SHAPE
+    assert call(flags=1 << 16) == _lib.ERR_BAD_SHAPE
     assert call(T=-1) == _lib.ERR_BAD_SHAPE
     assert call(D=80) == _lib.ERR_BAD_SHAPE
     assert call(mb=64) == _lib.ERR_BAD_SHAPE                 # table narrower than the context

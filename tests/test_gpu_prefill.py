@@ -64,6 +64,36 @@ def test_ragged_prompts_and_chunks(H, D):
     assert zero.sum() == 3 and not to_host(out)[zero].any()
 
 
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+@pytest.mark.parametrize("D", [64, 128])
+def test_heads_per_item_same_bits(D, sign):
+    """Items of 1, 2, 4 and 8 heads of one query group, the tile pipeline
+    running from one head into the next: with H = 6, items of 4 and 8 heads
+    end on a short head group.  Sequences of one pair of blocks per head
+    (the next head's queries load right after the first pair's score
+    products), of many pairs, of several query groups, an empty one, one
+    with more queries than tokens; both signs of the scale (the next head's
+    queries are negated as they come in).  The outputs are equal bit for bit
+    for every choice, and match the oracle."""
+    H = 6
+    lens = [37, 70, 16, 5, 9, 0, 33, 200, 400, 24, 32]
+    nq = [37, 20, 3, 5, 12, 0, 1, 77, 260, 24, 2]
+    q, kp, vp, tables, lens, qs = _ragged(60 + D, H, D, lens, nq)
+    scale = sign * float(np.float32(D ** -0.5))
+    kd, vd = to_dev(kp), to_dev(vp)
+    args = (to_dev(tables), to_dev(lens), to_dev(qs), scale)
+    outs = {}
+    for k in (1, 2, 4, 8):
+        print(f"prefill heads_per_item={k} D={D} sign={sign}", flush=True)
+        outs[k] = pa_prefill(to_dev(q), kd, vd, *args, max_context_len=int(lens.max()),
+                             heads_per_item=k)
+    torch.cuda.synchronize()
+    for k in (2, 4, 8):
+        assert torch.equal(outs[k].view(torch.int16), outs[1].view(torch.int16)), k
+    ref = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
+    assert_close(outs[4], ref, f"prefill, 4 heads per item, D={D}")
+
+
 def test_long_contexts():
     """Contexts past 256 blocks (more block ids than threads to stage them
     in one pass): a 200-row chunk over 4,800 cached tokens, one query at
@@ -126,6 +156,12 @@ def test_prompt_workload_append_then_prefill():
     assert np.array_equal(to_host(vp).view(np.uint16), v_ref.view(np.uint16))
     out = run_prefill(c.q, kp, vp, c.block_tables, c.context_lens, c.query_start, c.scale,
                       c.max_context)
+    # the default takes several heads per item here; one head per item gives
+    # the same bits
+    one = pa_prefill(to_dev(c.q), kp, vp, to_dev(c.block_tables), to_dev(c.context_lens),
+                     to_dev(c.query_start), c.scale, max_context_len=c.max_context,
+                     heads_per_item=1)
+    assert torch.equal(one.view(torch.int16), out.view(torch.int16))
     seqs = list(range(0, 200, 9)) + [199]
     ref = paged_prefill_ref(c.q, k_ref, v_ref, c.block_tables, c.context_lens, c.query_start,
                             c.scale, seqs=seqs)

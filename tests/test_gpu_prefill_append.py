@@ -98,6 +98,36 @@ def test_ragged_boundaries(H, D):
            f"ragged fused prefill H={H} D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_heads_per_item_same_bits(D):
+    """Items of 1, 2, 4 and 8 heads (H = 6: items of 4 and 8 end on a short
+    head group), new tokens on and off block boundaries, one pair of blocks
+    per head, several query groups owning blocks: pools and outputs equal bit
+    for bit for every choice, and the oracle's append and attention."""
+    H = 6
+    lens = [37, 70, 48, 5, 9, 0, 40, 200, 400, 399, 16, 30]
+    nq = [37, 20, 16, 12, 12, 0, 1, 200, 250, 8, 8, 30]
+    q, k_new, v_new, kp, vp, tables, lens, qs = _case(70 + D, H, D, lens, nq)
+    scale = float(np.float32(D ** -0.5))
+    res = {}
+    for k in (1, 2, 4, 8):
+        print(f"prefill_append heads_per_item={k} D={D}", flush=True)
+        kf, vf = to_dev(kp), to_dev(vp)
+        out = pa_prefill_append(to_dev(q), to_dev(k_new), to_dev(v_new), kf, vf, to_dev(tables),
+                                to_dev(lens), to_dev(qs), scale, max_context_len=int(lens.max()),
+                                heads_per_item=k)
+        torch.cuda.synchronize()
+        res[k] = (out, kf, vf)
+    for k in (2, 4, 8):
+        for a, b in zip(res[k], res[1]):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), k
+    k_ref, v_ref = append_ref(k_new, v_new, natural_slots(tables, lens, qs), kp, vp)
+    assert np.array_equal(to_host(res[8][1]).view(np.uint16), k_ref.view(np.uint16))
+    assert np.array_equal(to_host(res[8][2]).view(np.uint16), v_ref.view(np.uint16))
+    ref = paged_prefill_ref(q, k_ref, v_ref, tables, lens, qs, scale)
+    assert_close(res[8][0], ref, f"fused prefill, 8 heads per item, D={D}")
+
+
 def test_long_sequences_many_owners():
     """Contexts of thousands of tokens: a 700-token chunk starting inside a
     block (several query groups each own the blocks their rows start), a

@@ -164,9 +164,10 @@ def prefill_asm(tmp_path_factory):
     return device_asm("pa_prefill.hip", tmp_path_factory.mktemp("isa"))
 
 
+@pytest.mark.parametrize("multi", [False, True])
 @pytest.mark.parametrize("append", [False, True])
 @pytest.mark.parametrize("D", [128, 64])
-def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D, append):
+def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D, append, multi):
     """The prefill's tile loop: 32x32x16 MFMAs, the K/V buffer resources stay
     scalar (no waterfall loop around a load), and no wait drains the loads.
     Without the append, tiles are copied straight into LDS (buffer_load ...
@@ -174,8 +175,10 @@ def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D, append):
     in flight; with it, they come through a register ring in which three
     tiles (D/64 16-byte loads per thread and tile) stay in flight at every
     wait, through the per-tile choice of source (rows or pools) and the pool
-    writes."""
-    name = f"pa_prefill_kernelILi{D}ELb{int(append)}E"
+    writes.  Items of several heads (multi) run the same loops with the head
+    boundaries inside: there the ring's waits for the next head's queries
+    still leave the two tiles fetched last in flight."""
+    name = f"pa_prefill_kernelILi{D}ELb{int(append)}ELb{int(multi)}E"
     body = kernel_body(prefill_asm, name)
     # the ring is the loop with the most MFMAs (the item loop around it
     # holds the first pair's score products and waits for each item's start)
@@ -188,7 +191,7 @@ def test_prefill_ring_keeps_a_tile_in_flight(prefill_asm, D, append):
     assert "vmcnt(0)" not in ring
     waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", ring)]
     if append:
-        assert waits and min(waits) >= 3 * (D // 64)
+        assert waits and min(waits) >= (2 if multi else 3) * (D // 64)
     else:
         assert re.search(r"buffer_load_dwordx4 .* lds", ring)
         assert waits and min(waits) >= 2 * (D // 64)
