@@ -248,6 +248,13 @@ void pa_prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     sign_q();
     const int p_wave = p_group + 32 * wave;               // position of the wave's first row
+    // Causality per wave: a pair of blocks that starts past the wave's last
+    // row is masked for all its rows (an exact no-op), so the wave skips its
+    // arithmetic and leaves the matrix core to the other workgroup on its
+    // SIMD.  need(pp): pair pp of a head is not all masked for this wave
+    // (uniform per wave; false from some pp on).
+    const int p_wlast = p_group + min(32 * wave + 31, grows - 1);
+    auto need = [&](int pp) { return wave_rows && 2 * kBlockTokens * pp <= p_wlast; };
 
     float m = kNegInf, l = 0.0f;        // reference maximum (scaled, log2); sum over this lane's tokens
     f16x16 acc[kSl];
@@ -542,11 +549,9 @@ void pa_prefill_kernel(PrefillArgs a) {
       // The two halves of a round alternate the score registers (sc_a holds
       // pair p's scores on entry), so no copy joins them.
       f16x16 sc_a = {}, sc_b = {};
-      if (wave_rows) {
-        sc_a = scores(s_kv[0], s_kv[1]);
-        if constexpr (kMulti) {
-          if (npairs == 1 && nh > 1) load_q(h0 + 1);
-        }
+      if (need(0)) sc_a = scores(s_kv[0], s_kv[1]);
+      if constexpr (kMulti) {
+        if (wave_rows && npairs == 1 && nh > 1) load_q(h0 + 1);
       }
       int ch = 0, cp = 0;                                 // the pair computed now
       int sl = 0;                                         // its pair slot
@@ -561,16 +566,23 @@ void pa_prefill_kernel(PrefillArgs a) {
         stage_tile(ra + 1, 2 * sn + 1);
         fetch_tile(ra + 1, 1);
         __syncthreads();
-        if (wave_rows) {                                  // uniform per wave
-          if constexpr (kMulti) {
+        if constexpr (kMulti) {
+          if (wave_rows) {                                // uniform per wave
+            // a new head starts with the next pair: its first pair is needed
+            // even where this head's last pairs are not
             const bool cur_last = cp == npairs - 1;
-            const float mref = prep(cur, ch < nh ? cp : npairs);
-            if (cur_last && ch + 1 < nh) sign_q();
-            next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
+            const bool head_next = cur_last && ch + 1 < nh;
+            const bool need_cur = ch < nh && need(cp);
+            float mref = 0.0f;
+            if (need_cur) mref = prep(cur, cp);
+            if (head_next) sign_q();
+            if (need_cur || head_next) next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
             if (next_is_last(cp) && (cur_last ? ch + 1 : ch) + 1 < nh)
               load_q(h0 + (cur_last ? ch + 1 : ch) + 1);
-            weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
-          } else {
+            if (need_cur) weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
+          }
+        } else {
+          if (need(cp)) {                                 // uniform per wave
             const float mref = prep(cur, cp);
             next = scores(s_kv[2 * sn], s_kv[2 * sn + 1]);
             weights_pv(cur, mref, s_kv[2 * sl], s_kv[2 * sl + 1]);
@@ -643,14 +655,12 @@ void pa_prefill_kernel(PrefillArgs a) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       asm volatile("s_barrier" ::: "memory");
       f16x16 sc_a = {}, sc_b = {};
-      if (wave_rows) {
-        sc_a = scores(s_d0[0], s_d0[1]);
-        if constexpr (kMulti) {
-          // one pair per head: the next head's queries now
-          if (npairs == 1 && nh > 1) {
-            load_q(h0 + 1);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-          }
+      if (need(0)) sc_a = scores(s_d0[0], s_d0[1]);
+      if constexpr (kMulti) {
+        // one pair per head: the next head's queries now
+        if (wave_rows && npairs == 1 && nh > 1) {
+          load_q(h0 + 1);
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
       }
       int ch = 0, cp = 0;                                 // the pair computed now
@@ -659,7 +669,7 @@ void pa_prefill_kernel(PrefillArgs a) {
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kUnits) : "memory");
         if constexpr (!kMulti) {
           dma(free_slot);
-          if (wave_rows) {                                // uniform per wave
+          if (need(cp)) {                                 // uniform per wave
             const float mref = prep(cur, cp);
             next = scores(next_slot[0], next_slot[1]);
             weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
@@ -667,16 +677,18 @@ void pa_prefill_kernel(PrefillArgs a) {
         } else {
           if (cp == 0 && ch > 0 && wave_rows) finish(h0 + ch - 1);
           const bool cur_last = cp == npairs - 1;
+          const bool head_next = cur_last && ch + 1 < nh;
+          const bool need_cur = need(cp);
           const bool qnew = wave_rows && next_is_last(cp) && (cur_last ? ch + 1 : ch) + 1 < nh;
           float mref = 0.0f;
           if (wave_rows) {                                // uniform per wave
-            mref = prep(cur, cp);
-            if (cur_last && ch + 1 < nh) sign_q();
-            next = scores(next_slot[0], next_slot[1]);
+            if (need_cur) mref = prep(cur, cp);
+            if (head_next) sign_q();
+            if (need_cur || head_next) next = scores(next_slot[0], next_slot[1]);
             if (qnew) load_q(h0 + (cur_last ? ch + 1 : ch) + 1);
           }
           dma(free_slot);
-          if (wave_rows) weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
+          if (need_cur) weights_pv(cur, mref, cur_slot[0], cur_slot[1]);
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kUnits));
         }
         advance(ch, cp);
