@@ -265,23 +265,38 @@ void pa_prefill_kernel(PrefillArgs a) {
 
     // Output rows of head h from the sums, which then restart for the next
     // head.  Rows at a negative position (more queries than cached tokens)
-    // are zero; lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row.
+    // are zero.  Lane l holds dims 32s + 8q + 4hf .. +3 (q < 4) of its row;
+    // the two lanes of a row swap halves (one permlane32 swap per dword) so
+    // that each writes 16 contiguous bytes: of dims 32s + 16p .. +15, the
+    // lane with hf = 0 writes the first 8, the other the last 8.  Half as
+    // many store instructions and write requests as 8-byte pieces.  A lane
+    // without a row stores past the buffer's range (dropped).
+    const rsrc_t outr = make_rsrc(a.out, (uint32_t)((size_t)a.num_rows * a.H * D * 2));
     auto finish = [&](int h) {
       auto sw = __builtin_amdgcn_permlane32_swap(as_u32(l), as_u32(l), false, false);
       const float lt = as_f32(sw[0]) + as_f32(sw[1]);
-      if (row_ok) {
-        const float inv = p_q >= 0 && lt > 0.0f ? 1.0f / lt : 0.0f;
-        _Float16* orow = a.out + ((size_t)qrow * a.H + h) * D + 4 * hf;
+      const float inv = row_ok && p_q >= 0 && lt > 0.0f ? 1.0f / lt : 0.0f;
+      const uint32_t ob =
+          row_ok ? (uint32_t)((((size_t)qrow * a.H + h) * D + 8 * hf) * 2) : 0xFFFFFFF0u;
   #pragma unroll
-        for (int s = 0; s < kSl; ++s)
+      for (int s = 0; s < kSl; ++s)
   #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            h4v o;
+        for (int p = 0; p < 2; ++p) {
+          h4v lo, hi;                                     // dims 32s + 16p + 4hf, + 8
   #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = (_Float16)(acc[s][4 * q + r] * inv);
-            *reinterpret_cast<h4v*>(orow + 32 * s + 8 * q) = o;
+          for (int r = 0; r < 4; ++r) {
+            lo[r] = (_Float16)(acc[s][8 * p + r] * inv);
+            hi[r] = (_Float16)(acc[s][8 * p + 4 + r] * inv);
           }
-      }
+          typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+          const u2v lo2 = __builtin_bit_cast(u2v, lo), hi2 = __builtin_bit_cast(u2v, hi);
+          // lanes 32.. take the hf = 0 partner's hi, lanes .. 31 the partner's lo
+          auto x0 = __builtin_amdgcn_permlane32_swap(lo2[0], hi2[0], false, false);
+          auto x1 = __builtin_amdgcn_permlane32_swap(lo2[1], hi2[1], false, false);
+          const u4v o = {x0[0], x1[0], x0[1], x1[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(
+                o, outr, row_ok ? ob + (uint32_t)((32 * s + 16 * p) * 2) : 0xFFFFFFF0u, 0, 0);
+        }
       m = kNegInf;
       l = 0.0f;
   #pragma unroll
