@@ -122,6 +122,29 @@ def algorithmic_bytes(lens, H, D):
     return kv, kv + qo + tab
 
 
+def copy_probe(torch, dev, nbytes=1 << 30):
+    """Achievable read + write rate of a plain device copy (as many bytes
+    written as read: the mix of the prefill with its append fused in, which
+    reads q and the new rows and writes out and the pools), the best over a
+    few grid sizes of pkv_hbm_copy_probe, in GB/s of bytes read + written."""
+    from paged_kv_cache_03_amd.ops import hbm_copy_probe
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = 0.0
+    for w in (1024, 2048, 4096):
+        for _ in range(2):
+            hbm_copy_probe(src, dst, w)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(10):
+            hbm_copy_probe(src, dst, w)
+        e.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (s.elapsed_time(e) / 10 / 1e3) / 1e9)
+    del src, dst
+    return round(best, 1)
+
+
 def hbm_probe(torch, dev, nbytes=2 << 30):
     """Achievable HBM read rates next to the 8 TB/s published peak: a plain
     linear read, and a gather of 4 KiB chunks in random order (the decode's
@@ -1006,6 +1029,13 @@ def measure(torch, dev, wl, args, name, steps, warmup, cold_reps=0, probe=False,
         result["hbm_probe"] = hp
         result["roofline"]["achievable_gather_gbs"] = hp["gather_4k_gbs"]
         result["roofline"]["frac_of_achievable"] = round(achieved / hp["gather_4k_gbs"], 4)
+
+    if (name == "prefill_prompt" and pf is not None and pf["kernel"] == "pa_prefill_append"
+            and not args.no_hbm_probe):
+        # reads and writes in equal parts: the reference is a plain copy's rate
+        cp = copy_probe(torch, dev)
+        result["roofline"]["achievable_copy_gbs"] = cp
+        result["roofline"]["frac_of_achievable"] = round(result["roofline"]["achieved"] / cp, 4)
 
     if args.copy_probe:
         n = 1 << 30

@@ -485,11 +485,19 @@ size_t pkv_contig_decode_workspace_size(int32_t B, int32_t H, int32_t D,
  * entries are clamped into range), 16 KiB in flight per wave.  A random
  * permutation of 4 KiB chunks is the access pattern of 16-token blocks of
  * one 128-dim head scattered over a pool.
+ *
+ * pkv_hbm_copy_probe: copies `bytes` (a multiple of 16) from `src` to `dst`
+ * (device, 16-byte aligned, not overlapping) in one linear pass of 16-byte
+ * non-temporal loads and stores: as many bytes written as read, the
+ * read/write mix of a step that reads its inputs once and writes as much
+ * back (the prefill with its append fused in).
  */
 int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t workgroups,
                        void* stream);
 int pkv_hbm_gather_probe(const void* buf, size_t bytes, const int32_t* chunk_order,
                          int32_t chunk_bytes, void* sink, int32_t workgroups, void* stream);
+int pkv_hbm_copy_probe(const void* src, void* dst, size_t bytes, int32_t workgroups,
+                       void* stream);
 
 /* Static description of a status code. */
 const char* pkv_status_string(int code);

@@ -656,6 +656,16 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t workgr
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pkv_hbm_copy_probe(const void* src, void* dst, size_t bytes, int32_t workgroups,
+                       void* stream) {
+  if (bytes == 0 || bytes % 16 || workgroups <= 0) return PKV_ERR_BAD_SHAPE;
+  if (!src || !dst) return PKV_ERR_NULL_PTR;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return PKV_ERR_MISALIGNED;
+  const hipError_t e = pkv::launch_hbm_copy_probe(src, dst, (long long)(bytes / 16), workgroups,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pkv_hbm_gather_probe(const void* buf, size_t bytes, const int32_t* chunk_order,
                          int32_t chunk_bytes, void* sink, int32_t workgroups, void* stream) {
   int log_kib = -1;

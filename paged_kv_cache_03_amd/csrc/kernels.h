@@ -201,6 +201,8 @@ hipError_t launch_pa_decode(const PartArgs& part, int D, int grid_part, int thre
                             hipStream_t stream);
 hipError_t launch_pa_decode_flat(const FlatArgs& a, int D, int threads, hipStream_t stream);
 size_t flat_lds_bytes(int B, int max_chunk);
+hipError_t launch_hbm_copy_probe(const void* src, void* dst, long long n16, int grid,
+                                 hipStream_t stream);
 hipError_t launch_hbm_read_probe(const void* buf, long long n16, uint32_t* sink, int grid,
                                  hipStream_t stream);
 hipError_t launch_hbm_gather_probe(const void* buf, const int32_t* order, long long n_chunks,

@@ -1,13 +1,16 @@
-// HBM read-bandwidth probes for gfx950: the rates that plain reads reach on
-// this GPU, the references the decode kernel's block reads are compared with
-// (the 8 TB/s figure is the published peak, which no kernel reaches).
+// HBM bandwidth probes for gfx950: the rates that plain reads (and a plain
+// copy) reach on this GPU, the references the kernels' traffic is compared
+// with (the 8 TB/s figure is the published peak, which no kernel reaches).
 //
 //  * linear: a resident grid of workgroups walks the buffer in 16-byte
 //    non-temporal loads, four independent loads in flight per thread per
 //    step;
 //  * gather: the buffer is cut into equal chunks that are read in a given
 //    order (a random permutation stands for scattered pages), each wave
-//    keeping 16 KiB in flight, the depth the decode's three-tile ring keeps.
+//    keeping 16 KiB in flight, the depth the decode's three-tile ring keeps;
+//  * copy: a linear pass that writes every 16 bytes it reads to a second
+//    buffer (as many bytes written as read, the mix of a step that reads its
+//    inputs once and writes as much), non-temporal both ways.
 //
 // The loaded words are folded into one value that is stored only if it
 // equals a constant no real data produces, so the loads cannot be removed
@@ -73,7 +76,32 @@ __global__ __launch_bounds__(256) void hbm_gather_probe_kernel(const u4v* __rest
   if (acc == kNever) *sink = acc;
 }
 
+__global__ __launch_bounds__(256) void hbm_copy_probe_kernel(const u4v* __restrict__ src,
+                                                             u4v* __restrict__ dst,
+                                                             long long n16) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u4v a = __builtin_nontemporal_load(src + i);
+    const u4v b = __builtin_nontemporal_load(src + i + stride);
+    const u4v c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u4v d = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+    __builtin_nontemporal_store(c, dst + i + 2 * stride);
+    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+  }
+  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
+
+hipError_t launch_hbm_copy_probe(const void* src, void* dst, long long n16, int grid,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(hbm_copy_probe_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const u4v*>(src), static_cast<u4v*>(dst), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_hbm_read_probe(const void* buf, long long n16, uint32_t* sink, int grid,
                                  hipStream_t stream) {

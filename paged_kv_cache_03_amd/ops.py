@@ -528,6 +528,23 @@ def hbm_read_probe(buf, sink, workgroups=2048):
     _lib.check("pkv_hbm_read_probe", code)
 
 
+def hbm_copy_probe(src, dst, workgroups=2048):
+    """Copy ``src`` to ``dst`` (contiguous device tensors of the same
+    multiple of 16 bytes) in one linear pass of non-temporal loads and stores
+    (measurement aid: the read + write rate; see pkv_hbm_copy_probe)."""
+    lib = _lib.load_library()
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or dst.device != src.device:
+        raise ValueError("src and dst must have the same size, on one device")
+    with torch.cuda.device(src.device):
+        code = lib.pkv_hbm_copy_probe(_ptr(src), _ptr(dst), nbytes, workgroups,
+                                      _stream_handle(src.device))
+    _lib.check("pkv_hbm_copy_probe", code)
+
+
 def hbm_gather_probe(buf, order, chunk_bytes, sink, workgroups=512):
     """Read ``buf`` as chunks of ``chunk_bytes`` in the order of ``order``
     (int32 device tensor, one entry per chunk); measurement aid, see

@@ -210,6 +210,13 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.pkv_hbm_read_probe(A16, 32, A16, 0, None) == _lib.ERR_BAD_SHAPE
     assert lib.pkv_hbm_read_probe(None, 32, A16, 64, None) == _lib.ERR_NULL_PTR
     assert lib.pkv_hbm_read_probe(A4, 32, A16, 64, None) == _lib.ERR_MISALIGNED
+    c = lib.pkv_hbm_copy_probe
+    assert c(A16, A16, 0, 64, None) == _lib.ERR_BAD_SHAPE
+    assert c(A16, A16, 24, 64, None) == _lib.ERR_BAD_SHAPE
+    assert c(A16, A16, 32, 0, None) == _lib.ERR_BAD_SHAPE
+    assert c(None, A16, 32, 64, None) == _lib.ERR_NULL_PTR
+    assert c(A16, None, 32, 64, None) == _lib.ERR_NULL_PTR
+    assert c(A16, A4, 32, 64, None) == _lib.ERR_MISALIGNED
     g = lib.pkv_hbm_gather_probe
     assert g(A16, 0, A16, 4096, A16, 64, None) == _lib.ERR_BAD_SHAPE
     assert g(A16, 8192, A16, 3072, A16, 64, None) == _lib.ERR_BAD_SHAPE    # not a power of two

@@ -112,3 +112,19 @@ def test_debug_mode_rejects_contract_violations_before_launch():
         assert torch.equal(kp, k0) and torch.equal(vp, v0)
     finally:
         set_debug(old)
+
+
+def test_copy_probe_copies_every_byte():
+    """The copy probe (the read + write reference rate of the bench) copies
+    its source whole, the tail past the last full grid stride included, and
+    writes nothing past the end of its destination."""
+    from paged_kv_cache_03_amd.ops import hbm_copy_probe
+    n = (1 << 20) + 48
+    g = torch.Generator(device="cpu").manual_seed(5)
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g).to(dev())
+    dst = torch.zeros(n + 64, dtype=torch.uint8, device=dev())
+    print("copy probe", n, flush=True)
+    hbm_copy_probe(src, dst[:n], 64)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src)
+    assert not dst[n:].any()
