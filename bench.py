@@ -131,7 +131,7 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     best = 0.0
-    for w in (1024, 2048, 4096):
+    for w in (1024, 4096, 16384):
         for _ in range(2):
             hbm_copy_probe(src, dst, w)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

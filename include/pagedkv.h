@@ -487,10 +487,10 @@ size_t pkv_contig_decode_workspace_size(int32_t B, int32_t H, int32_t D,
  * one 128-dim head scattered over a pool.
  *
  * pkv_hbm_copy_probe: copies `bytes` (a multiple of 16) from `src` to `dst`
- * (device, 16-byte aligned, not overlapping) in one linear pass of 16-byte
- * non-temporal loads and stores: as many bytes written as read, the
- * read/write mix of a step that reads its inputs once and writes as much
- * back (the prefill with its append fused in).
+ * (device, 16-byte aligned, not overlapping), each of the `workgroups`
+ * workgroups over a contiguous slice, 16-byte non-temporal loads: as many
+ * bytes written as read, the read/write mix of a step that reads its inputs
+ * once and writes as much back (the prefill with its append fused in).
  */
 int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t workgroups,
                        void* stream);

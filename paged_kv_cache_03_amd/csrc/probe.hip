@@ -8,9 +8,9 @@
 //  * gather: the buffer is cut into equal chunks that are read in a given
 //    order (a random permutation stands for scattered pages), each wave
 //    keeping 16 KiB in flight, the depth the decode's three-tile ring keeps;
-//  * copy: a linear pass that writes every 16 bytes it reads to a second
-//    buffer (as many bytes written as read, the mix of a step that reads its
-//    inputs once and writes as much), non-temporal both ways.
+//  * copy: every 16 bytes read are written to a second buffer (as many bytes
+//    written as read, the mix of a step that reads its inputs once and writes
+//    as much), each workgroup over a contiguous slice, non-temporal loads.
 //
 // The loaded words are folded into one value that is stored only if it
 // equals a constant no real data produces, so the loads cannot be removed
@@ -76,30 +76,36 @@ __global__ __launch_bounds__(256) void hbm_gather_probe_kernel(const u4v* __rest
   if (acc == kNever) *sink = acc;
 }
 
+// Each workgroup copies its own contiguous slice of `per` units, 4 units per
+// thread in flight (faster than a grid-stride walk of the whole buffer on
+// this GPU: 5.3-5.4 against 4.4-5.1 TB/s read + write for 1 GiB).
 __global__ __launch_bounds__(256) void hbm_copy_probe_kernel(const u4v* __restrict__ src,
                                                              u4v* __restrict__ dst,
-                                                             long long n16) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u4v a = __builtin_nontemporal_load(src + i);
-    const u4v b = __builtin_nontemporal_load(src + i + stride);
-    const u4v c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u4v d = __builtin_nontemporal_load(src + i + 3 * stride);
-    __builtin_nontemporal_store(a, dst + i);
-    __builtin_nontemporal_store(b, dst + i + stride);
-    __builtin_nontemporal_store(c, dst + i + 2 * stride);
-    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+                                                             long long n16, long long per) {
+  const long long b0 = (long long)blockIdx.x * per;
+  const long long b1 = b0 + per < n16 ? b0 + per : n16;
+  for (long long i = b0 + threadIdx.x; i < b1; i += 4 * 256) {
+    u4v v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long long j = i + 256 * k;
+      v[k] = j < b1 ? __builtin_nontemporal_load(src + j) : u4v{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long long j = i + 256 * k;
+      if (j < b1) dst[j] = v[k];
+    }
   }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
 
 hipError_t launch_hbm_copy_probe(const void* src, void* dst, long long n16, int grid,
                                  hipStream_t stream) {
+  const long long per = (n16 + grid - 1) / grid;
   hipLaunchKernelGGL(hbm_copy_probe_kernel, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const u4v*>(src), static_cast<u4v*>(dst), n16);
+                     static_cast<const u4v*>(src), static_cast<u4v*>(dst), n16, per);
   return hipGetLastError();
 }
 

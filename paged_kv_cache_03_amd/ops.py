@@ -528,9 +528,9 @@ def hbm_read_probe(buf, sink, workgroups=2048):
     _lib.check("pkv_hbm_read_probe", code)
 
 
-def hbm_copy_probe(src, dst, workgroups=2048):
+def hbm_copy_probe(src, dst, workgroups=4096):
     """Copy ``src`` to ``dst`` (contiguous device tensors of the same
-    multiple of 16 bytes) in one linear pass of non-temporal loads and stores
+    multiple of 16 bytes), each workgroup over a contiguous slice
     (measurement aid: the read + write rate; see pkv_hbm_copy_probe)."""
     lib = _lib.load_library()
     for t, name in ((src, "src"), (dst, "dst")):

@@ -76,8 +76,8 @@ def test_heads_per_item_same_bits(D, sign):
     queries are negated as they come in).  The outputs are equal bit for bit
     for every choice, and match the oracle."""
     H = 6
-    lens = [37, 70, 16, 5, 9, 0, 33, 200, 400, 24, 32]
-    nq = [37, 20, 3, 5, 12, 0, 1, 77, 260, 24, 2]
+    lens = [37, 70, 16, 5, 9, 0, 33, 200, 400, 24, 32, 0]
+    nq = [37, 20, 3, 5, 12, 0, 1, 77, 260, 24, 2, 5]   # the last: no cached token, 5 rows
     q, kp, vp, tables, lens, qs = _ragged(60 + D, H, D, lens, nq)
     scale = sign * float(np.float32(D ** -0.5))
     kd, vd = to_dev(kp), to_dev(vp)
@@ -92,6 +92,7 @@ def test_heads_per_item_same_bits(D, sign):
         assert torch.equal(outs[k].view(torch.int16), outs[1].view(torch.int16)), k
     ref = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
     assert_close(outs[4], ref, f"prefill, 4 heads per item, D={D}")
+    assert not to_host(outs[8])[qs[-2]:].any()          # rows with no position: zero
 
 
 def test_long_contexts():

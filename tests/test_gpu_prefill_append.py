@@ -105,8 +105,8 @@ def test_heads_per_item_same_bits(D):
     per head, several query groups owning blocks: pools and outputs equal bit
     for bit for every choice, and the oracle's append and attention."""
     H = 6
-    lens = [37, 70, 48, 5, 9, 0, 40, 200, 400, 399, 16, 30]
-    nq = [37, 20, 16, 12, 12, 0, 1, 200, 250, 8, 8, 30]
+    lens = [37, 70, 48, 5, 9, 0, 40, 200, 400, 399, 16, 30, 0]
+    nq = [37, 20, 16, 12, 12, 0, 1, 200, 250, 8, 8, 30, 4]   # the last: rows, no position
     q, k_new, v_new, kp, vp, tables, lens, qs = _case(70 + D, H, D, lens, nq)
     scale = float(np.float32(D ** -0.5))
     res = {}
