@@ -191,10 +191,20 @@ void pa_prefill_kernel(PrefillArgs a) {
     const int gt = item / hgroups;
     const int h0 = (item - gt * hgroups) * hpi;
     const int nh = kMulti ? min(hpi, a.H - h0) : 1;
-    const int b = seq_of_group(s_group, a.B, gt);
-    const int n = rows_of(a, b);
-    const int kq = groups_of(a, b) - 1 - (gt - s_group[b]);   // furthest-reaching group first
-    const int ctx = clampi(a.context_lens[b], 0, a.ctx_limit);
+    // (the item's parameters are the same for every lane: taken as uniform,
+    // so that they live in scalar registers and are not loaded again)
+    const int b = __builtin_amdgcn_readfirstlane(seq_of_group(s_group, a.B, gt));
+    // The first blockDim.x entries of the sequence's block table, loaded
+    // before the sequence's lengths are known (both depend only on b), so
+    // the two loads overlap instead of following each other; entries past
+    // the item's blocks are not used.
+    const int cap = min(a.max_blocks, (a.ctx_limit + kBlockTokens - 1) / kBlockTokens);
+    const int id_first = tid < cap ? a.block_tables[(size_t)b * a.max_blocks + tid] : 0;
+    const int qs_b = __builtin_amdgcn_readfirstlane(a.query_start[b]);
+    const int n = max(0, __builtin_amdgcn_readfirstlane(a.query_start[b + 1]) - qs_b);
+    const int kq = (n + kPrefillRows - 1) / kPrefillRows - 1 -
+                   (gt - __builtin_amdgcn_readfirstlane(s_group[b]));   // furthest-reaching first
+    const int ctx = clampi(__builtin_amdgcn_readfirstlane(a.context_lens[b]), 0, a.ctx_limit);
     const int row0 = kPrefillRows * kq;
     const int grows = min(kPrefillRows, n - row0);
     const int p_group = ctx - n + row0;                   // position of the group's first row
@@ -208,7 +218,7 @@ void pa_prefill_kernel(PrefillArgs a) {
     // Block ids, clamped into the pool for reading.  With the append, an
     // entry outside the pool also sets bit 31, so the block is never written.
     for (int j = tid; j < nblk; j += blockDim.x) {
-      const int id = a.block_tables[(size_t)b * a.max_blocks + j];
+      const int id = j == tid ? id_first : a.block_tables[(size_t)b * a.max_blocks + j];
       const int in_pool = clampi(id, 0, a.num_blocks - 1);
       s_ids[j] = kAppend && in_pool != id ? (int)((uint32_t)in_pool | 0x80000000u) : in_pool;
     }
@@ -218,7 +228,7 @@ void pa_prefill_kernel(PrefillArgs a) {
     // row skips the arithmetic (it still loads, stages and meets the barriers)
     const bool wave_rows = 32 * wave < grows;
     const int wrow = 32 * wave + col;
-    const int qrow = a.query_start[b] + row0 + wrow;
+    const int qrow = qs_b + row0 + wrow;
     const bool row_ok = wrow < grows && qrow >= 0 && qrow < a.num_rows;
     const int p_q = p_group + wrow;
     const rsrc_t qr = make_rsrc(a.q, (uint32_t)((size_t)a.num_rows * a.H * D * 2));
@@ -243,10 +253,6 @@ void pa_prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < kQK; ++i) qb[i] = -qb[i];
       }
     };
-    load_q(h0);
-    // keep the query loads ahead of the ring's first tiles (every step reads them)
-    __builtin_amdgcn_sched_barrier(0);
-    sign_q();
     const int p_wave = p_group + 32 * wave;               // position of the wave's first row
     // Causality per wave: a pair of blocks that starts past the wave's last
     // row is masked for all its rows (an exact no-op), so the wave skips its
@@ -326,7 +332,7 @@ void pa_prefill_kernel(PrefillArgs a) {
     const int u_r = tid % kTileUnits;
     const int t_r = u_r % kBlockTokens;
     const int g_r = u_r / kBlockTokens;
-    const int row_r = a.query_start[b] - bnd + t_r;
+    const int row_r = qs_b - bnd + t_r;
     const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
     const uint32_t rows_total = (uint32_t)a.num_rows * row_bytes;
     // byte offset of token t_r of block 0, head h0 (modulo 2^32: row_r may
@@ -556,6 +562,10 @@ void pa_prefill_kernel(PrefillArgs a) {
       auto stage_tile = [&](int r, int st) { stage(ring[r], st, ring_j[r], ring_h[r], ring_o[r]); };
   #pragma unroll
       for (int r = 0; r < R; ++r) fetch_tile(r, r % 2);
+      // the queries after the first tiles, whose latency the item's start
+      // waits out (the compiler waits for them before the first products)
+      load_q(h0);
+      sign_q();
       stage_tile(0, 0);
       stage_tile(1, 1);
       fetch_tile(0, 0);
@@ -663,6 +673,10 @@ void pa_prefill_kernel(PrefillArgs a) {
       dma(s_d0);
       dma(s_d1);
       dma(s_d2);
+      // the queries after the first copies (issued first, the copies would
+      // queue behind them); the wait below covers both
+      load_q(h0);
+      sign_q();
       // The first three pairs complete (issued together, they land close
       // together; the compiler would place this wait before the first LDS
       // read on its own, since it does not tell the copies issued here
