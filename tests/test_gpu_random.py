@@ -3,8 +3,9 @@ prefill, the append and the copy-on-write), against the oracle.
 
 Batch sizes, head counts (1-, 2- and 4-wave workgroups), head dims, context
 mixes (empty, one token, block edges, a few thousand tokens), partition
-lengths, cache policies and groupings are drawn from fixed seeds, so every
-run checks the same cases.  Slots no query may read hold NaN."""
+lengths, cache policies, groupings and the prefill's heads per work item are
+drawn from fixed seeds, so every run checks the same cases.  Slots no query
+may read hold NaN."""
 
 import numpy as np
 import pytest
@@ -155,13 +156,17 @@ def test_random_prefill(seed):
     tables, NB = _tables(rng, lens, int(rng.integers(0, 2)))
     c = _case(rng, B, H, D, lens, tables, NB)
     q = wl.normal_fp16(rng, (max(int(qs[-1]), 1), H, D))[:int(qs[-1])]
-    what = f"seed={seed} B={B} H={H} D={D} rows={int(qs[-1])}"
+    hpi = (None, 1, 2, 4, 8)[seed % 5]                # heads per work item
+    what = f"seed={seed} B={B} H={H} D={D} rows={int(qs[-1])} heads_per_item={hpi}"
     print(what, flush=True)
     if qs[-1] == 0:
         return
-    out = pa_prefill(to_dev(q), to_dev(c.k_pool), to_dev(c.v_pool), to_dev(tables), to_dev(lens),
-                     to_dev(qs), c.scale, max_context_len=int(max(lens.max(), 1)))
+    args = (to_dev(q), to_dev(c.k_pool), to_dev(c.v_pool), to_dev(tables), to_dev(lens),
+            to_dev(qs), c.scale)
+    out = pa_prefill(*args, max_context_len=int(max(lens.max(), 1)), heads_per_item=hpi)
+    one = pa_prefill(*args, max_context_len=int(max(lens.max(), 1)), heads_per_item=1)
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), one.view(torch.int16)), what
     assert_close(out, paged_prefill_ref(q, c.k_pool, c.v_pool, tables, lens, qs, c.scale), what)
 
 
@@ -183,7 +188,8 @@ def test_random_prefill_append(seed):
     c = _case(rng, B, H, D, lens, tables, NB)
     T = int(qs[-1])
     q, kn, vn = (wl.normal_fp16(rng, (max(T, 1), H, D))[:T] for _ in range(3))
-    what = f"seed={seed} B={B} H={H} D={D} rows={T}"
+    hpi = (8, 4, 2, None, 1)[seed % 5]                # heads per work item
+    what = f"seed={seed} B={B} H={H} D={D} rows={T} heads_per_item={hpi}"
     print(what, flush=True)
     if T == 0:
         return
@@ -194,7 +200,7 @@ def test_random_prefill_append(seed):
     kp, vp = to_dev(c.k_pool), to_dev(c.v_pool)
     out = pa_prefill_append(to_dev(q), to_dev(kn), to_dev(vn), kp, vp, to_dev(tables),
                             to_dev(lens), to_dev(qs), c.scale,
-                            max_context_len=int(max(lens.max(), 1)))
+                            max_context_len=int(max(lens.max(), 1)), heads_per_item=hpi)
     torch.cuda.synchronize()
     k_ref, v_ref = append_ref(kn, vn, slots, c.k_pool, c.v_pool)
     assert np.array_equal(to_host(kp).view(np.uint16), k_ref.view(np.uint16)), what
