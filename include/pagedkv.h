@@ -333,8 +333,10 @@ size_t pkv_pa_decode_grouped_workspace_size(int32_t B, int32_t H, int32_t D,
  * host:   sizes, scale, max_context_len (>= every context_lens[b]; contexts
  *         are clamped to it), block_size 16, flags 0 or
  *         PKV_PREFILL_HEADS_PER_ITEM(k).  The block ids of one sequence are
- *         staged in LDS: (B + 1 + max_context_len / 16) * 4 bytes must not
- *         exceed 32 KiB.  No workspace.
+ *         staged in LDS after a table of B + 1 entries, from an even entry
+ *         and with one spare: (E + ceil(max_context_len / 16) + 1) * 4 bytes,
+ *         E = B + 1 rounded up to even, must not exceed 32 KiB.  No
+ *         workspace.
  *
  * Work decomposition: a workgroup takes 128 query rows of one sequence for
  * k heads at a time (k = 1, 2, 4 or 8), and streams the sequence's blocks

@@ -157,7 +157,7 @@ void pa_prefill_kernel(PrefillArgs a) {
   // block also writes it to the pools.
   constexpr bool kDma = !kAppend;
   static_assert(!kDma || kLoaders == kThreads, "every thread copies a share of each pair");
-  extern __shared__ int smem[];
+  extern __shared__ __attribute__((aligned(16))) int smem[];
   __shared__ int s_wave[kPrefillWaves];
   // register-ring staging: three pair slots, each its K tile then V tile
   __shared__ u4v s_kv[kDma ? 1 : 2 * kSlots][kDma ? 1 : 2 * kTileUnits];
@@ -169,7 +169,9 @@ void pa_prefill_kernel(PrefillArgs a) {
   __shared__ u4v s_d2[kDma ? 2 : 1][kDma ? 2 * kTileUnits : 1];
   __shared__ u4v s_d3[kDma ? 2 : 1][kDma ? 2 * kTileUnits : 1];
   int* s_group = smem;                                  // B + 1
-  int* s_ids = smem + a.B + 1;                          // block ids of the sequence
+  // block ids of the sequence, 8-byte aligned with one spare entry, so that
+  // the two ids of a pair of blocks are read together
+  int* s_ids = smem + ((a.B + 2) & ~1);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -217,8 +219,9 @@ void pa_prefill_kernel(PrefillArgs a) {
 
     // Block ids, clamped into the pool for reading.  With the append, an
     // entry outside the pool also sets bit 31, so the block is never written.
-    for (int j = tid; j < nblk; j += blockDim.x) {
-      const int id = j == tid ? id_first : a.block_tables[(size_t)b * a.max_blocks + j];
+    // The entry after the last block is block 0 (read with the last pair).
+    for (int j = tid; j <= nblk; j += blockDim.x) {
+      const int id = j == nblk ? 0 : j == tid ? id_first : a.block_tables[(size_t)b * a.max_blocks + j];
       const int in_pool = clampi(id, 0, a.num_blocks - 1);
       s_ids[j] = kAppend && in_pool != id ? (int)((uint32_t)in_pool | 0x80000000u) : in_pool;
     }
@@ -642,13 +645,17 @@ void pa_prefill_kernel(PrefillArgs a) {
       int fh = 0, fp = 0;                                 // the pair copied next
       auto dma = [&](u4v (*slot)[2 * kTileUnits]) {
         const bool live = !kMulti || fh < nh;             // uniform
+        // both ids of the pair in one LDS read (a pair past the end reads the
+        // last one again; the spare entry after the blocks holds pool block 0,
+        // and copies past the blocks have an empty range)
+        const int j0 = 2 * min(fp, (nblk - 1) / 2);
+        const int ids[2] = {s_ids[j0], s_ids[j0 + 1]};
   #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int j = 2 * fp + hb;
-          const int jj = min(j, nblk - 1);
           const uint32_t bytes = live && j < nblk ? kTile : 0u;
-          const size_t o = (size_t)__builtin_amdgcn_readfirstlane(s_ids[jj]) * block_stride +
-                           (size_t)fh * kTile;
+          const int id = __builtin_amdgcn_readfirstlane(ids[hb]);
+          const size_t o = (size_t)id * block_stride + (size_t)fh * kTile;
   #pragma unroll
           for (int k = 0; k < kUnits; ++k) {
             // this wave's 64 consecutive slot positions of copy k: K units
@@ -782,7 +789,7 @@ __global__ __launch_bounds__(256) void prefill_boundary_append_kernel(PrefillArg
 }  // namespace
 
 size_t prefill_lds_bytes(int B, int max_blocks_used) {
-  return (size_t)(B + 1 + max_blocks_used) * sizeof(int);
+  return (size_t)(((B + 2) & ~1) + max_blocks_used + 1) * sizeof(int);
 }
 
 namespace {
