@@ -115,14 +115,26 @@ __device__ void group_prefix(const PrefillArgs& a, int* s_group, int* s_wave) {
   __syncthreads();
 }
 
+// The sequence of query group t: the largest b < B with s_group[b] <= t.
+// The whole wave searches, 64 candidates a round (one LDS read each and a
+// ballot): the answer stays in [lo, lo + len), where s_group[lo] <= t, and
+// since s_group does not decrease, the candidates that pass form a prefix
+// of the lanes.  B <= 4096 takes at most two rounds.  Uniform result; every
+// lane of the wave must be active.
 __device__ __forceinline__ int seq_of_group(const int* s_group, int B, int t) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_group[mid] <= t) lo = mid;
-    else hi = mid - 1;
+  const int lane = threadIdx.x % kWave;
+  int lo = 0, len = B;
+  while (len > 1) {
+    const int step = (len + kWave - 1) / kWave;
+    const int c = lo + step * lane;
+    const bool pass = c < lo + len && s_group[min(c, lo + len - 1)] <= t;
+    const uint64_t m = __ballot(pass);
+    const int k = 63 - __clzll(m | 1ull);                // the last lane that passes
+    const int c0 = lo + step * k;
+    len = min(step, lo + len - c0);
+    lo = c0;
   }
-  return lo;
+  return __builtin_amdgcn_readfirstlane(lo);
 }
 
 // Two waves per SIMD (two workgroups per CU): the register budget that
@@ -189,24 +201,45 @@ void pa_prefill_kernel(PrefillArgs a) {
   const int hpi = a.heads_per_item;
   const int hgroups = (a.H + hpi - 1) / hpi;
   const int items = s_group[a.B] * hgroups;
+  // An item's sequence, the first blockDim.x entries of its block table and
+  // its lengths.  With direct staging they are loaded one item ahead, while
+  // the item before waits for its first copies, so that their latency is
+  // not paid at the item's start.  Entries past the item's blocks are not
+  // used.  nx_len: lane 0 holds the sequence's first query row, lane 1 the
+  // end of its rows, the other lanes its context length (one vector load).
+  // Every path through an item issues these loads once and waits for them
+  // with the item's first copies, so that the compiler's wait for them at
+  // the next item's start leaves the item's output stores in flight.
+  const int cap = min(a.max_blocks, (a.ctx_limit + kBlockTokens - 1) / kBlockTokens);
+  int nx_b = 0, nx_id = 0, nx_len = 0;
+  // (past the last item, the last item's again: the loads are issued on
+  // every path, so the compiler's count of the loads in flight stays exact)
+  auto load_item = [&](int it) {
+    nx_b = seq_of_group(s_group, a.B, max(0, min(it, items - 1)) / hgroups);
+    nx_id = tid < cap ? a.block_tables[(size_t)nx_b * a.max_blocks + tid] : 0;
+    const int lane = tid % kWave;
+    nx_len = lane < 2 ? a.query_start[nx_b + lane] : a.context_lens[nx_b];
+  };
+  if constexpr (kDma) {
+    load_item(blockIdx.x);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    // (the register ring loads its item's at the start: loaded one item
+    // ahead there, its loop compiles to a slower schedule)
+    if constexpr (!kDma) load_item(item);
     const int gt = item / hgroups;
     const int h0 = (item - gt * hgroups) * hpi;
     const int nh = kMulti ? min(hpi, a.H - h0) : 1;
     // (the item's parameters are the same for every lane: taken as uniform,
-    // so that they live in scalar registers and are not loaded again)
-    const int b = __builtin_amdgcn_readfirstlane(seq_of_group(s_group, a.B, gt));
-    // The first blockDim.x entries of the sequence's block table, loaded
-    // before the sequence's lengths are known (both depend only on b), so
-    // the two loads overlap instead of following each other; entries past
-    // the item's blocks are not used.
-    const int cap = min(a.max_blocks, (a.ctx_limit + kBlockTokens - 1) / kBlockTokens);
-    const int id_first = tid < cap ? a.block_tables[(size_t)b * a.max_blocks + tid] : 0;
-    const int qs_b = __builtin_amdgcn_readfirstlane(a.query_start[b]);
-    const int n = max(0, __builtin_amdgcn_readfirstlane(a.query_start[b + 1]) - qs_b);
+    // so that they live in scalar registers)
+    const int b = nx_b;
+    const int id_first = nx_id;
+    const int qs_b = __builtin_amdgcn_readlane(nx_len, 0);
+    const int n = max(0, __builtin_amdgcn_readlane(nx_len, 1) - qs_b);
     const int kq = (n + kPrefillRows - 1) / kPrefillRows - 1 -
                    (gt - __builtin_amdgcn_readfirstlane(s_group[b]));   // furthest-reaching first
-    const int ctx = clampi(__builtin_amdgcn_readfirstlane(a.context_lens[b]), 0, a.ctx_limit);
+    const int ctx = clampi(__builtin_amdgcn_readlane(nx_len, 2), 0, a.ctx_limit);
     const int row0 = kPrefillRows * kq;
     const int grows = min(kPrefillRows, n - row0);
     const int p_group = ctx - n + row0;                   // position of the group's first row
@@ -220,11 +253,15 @@ void pa_prefill_kernel(PrefillArgs a) {
     // Block ids, clamped into the pool for reading.  With the append, an
     // entry outside the pool also sets bit 31, so the block is never written.
     // The entry after the last block is block 0 (read with the last pair).
-    for (int j = tid; j <= nblk; j += blockDim.x) {
-      const int id = j == nblk ? 0 : j == tid ? id_first : a.block_tables[(size_t)b * a.max_blocks + j];
+    // (the entries past the first blockDim.x are loaded here, in a loop of
+    // their own, so that the compiler's wait for them stays inside it)
+    auto put_id = [&](int j, int id) {
       const int in_pool = clampi(id, 0, a.num_blocks - 1);
       s_ids[j] = kAppend && in_pool != id ? (int)((uint32_t)in_pool | 0x80000000u) : in_pool;
-    }
+    };
+    if (tid <= nblk) put_id(tid, tid == nblk ? 0 : id_first);
+    for (int j = tid + blockDim.x; j <= nblk; j += blockDim.x)
+      put_id(j, j == nblk ? 0 : a.block_tables[(size_t)b * a.max_blocks + j]);
     __syncthreads();
 
     // this lane's query row: wave w serves rows row0 + 32w ..; a wave with no
@@ -683,6 +720,7 @@ void pa_prefill_kernel(PrefillArgs a) {
       // the queries after the first copies (issued first, the copies would
       // queue behind them); the wait below covers both
       load_q(h0);
+      load_item(item + gridDim.x);                        // the next item's, while these land
       sign_q();
       // The first three pairs complete (issued together, they land close
       // together; the compiler would place this wait before the first LDS
@@ -745,6 +783,10 @@ void pa_prefill_kernel(PrefillArgs a) {
       finish(h0 + nh - 1);
     } else {
       // no token to attend: every head's rows are zero
+      if constexpr (kDma) {
+        load_item(item + gridDim.x);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      }
       for (int hl = 0; hl < nh; ++hl) finish(h0 + hl);
     }
 

@@ -107,6 +107,24 @@ def test_long_contexts():
     assert_close(out, paged_prefill_ref(q, kp, vp, tables, lens, qs, scale), "long prefill")
 
 
+def test_thousands_of_sequences_many_without_rows():
+    """5,000 short sequences, a third of them with no query rows: the
+    search that finds an item's sequence among the query groups takes three
+    rounds of 64 candidates past 4,096 sequences, and skips the sequences
+    that own no group; each workgroup takes several items, whose sequence
+    and lengths are loaded one item ahead."""
+    rng = np.random.default_rng(91)
+    B = 5000
+    lens = rng.integers(0, 41, size=B)
+    nq = np.minimum(lens, rng.integers(1, 4, size=B))
+    nq[rng.random(B) < 0.33] = 0
+    q, kp, vp, tables, lens, qs = _ragged(91, 2, 64, list(lens), list(nq))
+    scale = float(np.float32(64 ** -0.5))
+    out = run_prefill(q, to_dev(kp), to_dev(vp), tables, lens, qs, scale, int(lens.max()))
+    ref = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
+    assert_close(out, ref, "prefill over 5,000 sequences")
+
+
 @pytest.mark.parametrize("mult", [1.0, -1.0, 0.0, 4.0])
 def test_scale_sign_zero_and_rising_scores(mult):
     """Keys that grow along the sequence (scores rise, so the online
