@@ -11,11 +11,12 @@
 // one head; each of its 4 waves serves 32 of them.  The workgroup streams
 // the blocks up to the one holding its last row's position once: every
 // (block, head) tile of K and V is fetched by the workgroup's threads
-// together (16 bytes each) through a register ring of four tiles and stored
-// into one of three LDS pair slots (V slots past the context zeroed, V
-// token slots swizzled against bank conflicts); after every second tile a
-// barrier, then each wave consumes the pair (32 tokens), its score products
-// issued one pair ahead of its softmax, on the
+// together (16 bytes each), copied straight from memory into one of four
+// LDS pair slots (buffer_load ... lds) or, with the append fused in,
+// through a register ring of four tiles into one of three (V slots past the
+// context zeroed, V token slots swizzled against bank conflicts); after
+// every pair of tiles a barrier, then each wave consumes the pair (32
+// tokens), its score products issued one pair ahead of its softmax, on the
 // v_mfma_f32_32x32x16_f16 matrix instruction, whose lane l holds row l%32
 // and k slots 8*(l/32) .. +7 of A, the same of B (column l%32), and C rows
 // 8*(r/4) + 4*(l/32) + r%4 of column l%32 in its register r:
