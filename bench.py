@@ -56,6 +56,9 @@ def parse(argv=None):
                     help="default workload only: skip timing the other workloads (batch 10, "
                          "shared prefix, full step, 4-beam step, both prefills) in the same run")
     ap.add_argument("--cpu-worker", metavar="DIR", help=argparse.SUPPRESS)
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only time the LDS read probe (one workgroup per CU, both read forms) "
+                         "and print its rates as one JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     ap.add_argument("--decode", choices=["auto", "flat", "grouped"], default="auto",
@@ -120,6 +123,40 @@ def algorithmic_bytes(lens, H, D):
     qo = len(lens) * H * D * 2 * 2
     tab = sum(4 * math.ceil(n / 16) + 4 for n in lens)
     return kv, kv + qo + tab
+
+
+def lds_probe(torch, dev, rounds=4000):
+    """LDS read rate per CU with pkv_lds_read_probe: one workgroup per CU of
+    4, 8 or 16 waves, each wave reading 64 KiB of LDS `rounds` times in 16-byte
+    row reads (form 0, 16 KiB per round) or in the prefill's transpose reads
+    (form 1, 8 KiB per round).  Bytes per shader clock per CU from each
+    workgroup's slowest wave (median over the CUs), the clock from the same
+    cycles over the launch's event time."""
+    import numpy as np
+    from paged_kv_cache_03_amd.ops import lds_read_probe
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {"rounds": rounds, "workgroups": cus}
+    for form, per_round in ((0, 16 * 1024), (1, 8 * 1024)):
+        for waves in (4, 8, 16):
+            cyc = torch.zeros(cus * waves, dtype=torch.int64, device=dev)
+            sink = torch.zeros(cus * waves, dtype=torch.int32, device=dev)
+            lds_read_probe(cyc, sink, cus, waves, 10, form)
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            lds_read_probe(cyc, sink, cus, waves, rounds, form)
+            e.record()
+            torch.cuda.synchronize()
+            us = s.elapsed_time(e) * 1e3
+            wg = cyc.cpu().numpy().reshape(cus, waves).max(axis=1)
+            bpc = waves * rounds * per_round / wg
+            out[f"form{form}_waves{waves}"] = {
+                "bytes_per_clock_per_cu": round(float(np.median(bpc)), 1),
+                "min": round(float(bpc.min()), 1), "max": round(float(bpc.max()), 1),
+                "instructions_per_clock_per_cu": round(float(np.median(bpc)) / (per_round / 16), 3),
+                "us": round(us, 1), "clock_ghz": round(float(np.median(wg)) / us / 1e3, 3)}
+            log(f"lds probe form {form} waves {waves}: {out[f'form{form}_waves{waves}']}")
+    return out
 
 
 def copy_probe(torch, dev, nbytes=1 << 30):
@@ -1086,6 +1123,9 @@ def main():
     dev = torch.device("cuda:0")
     log(f"device {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")
+    if args.lds_probe:
+        print(json.dumps({"lds_read_probe": lds_probe(torch, dev)}), flush=True)
+        return
 
     headline = args.workload == "batch200"
     result = measure(torch, dev, wl, args, args.workload, args.steps, args.warmup,

@@ -501,6 +501,25 @@ int pkv_hbm_gather_probe(const void* buf, size_t bytes, const int32_t* chunk_ord
 int pkv_hbm_copy_probe(const void* src, void* dst, size_t bytes, int32_t workgroups,
                        void* stream);
 
+/*
+ * pkv_lds_read_probe: the rate at which a CU reads its LDS, with the read
+ * forms of the prefill's pair loop ("PagedAttention", e-fortepiano.pl,
+ * "Formulació matemàtica": the block-by-block products read every K and V
+ * tile from LDS once per 32 query rows).  `workgroups` workgroups of `waves`
+ * waves (1..16), one per CU (each holds 96 KiB of LDS), fill 64 KiB of LDS
+ * and then read it `rounds` times per wave, conflict-free: form 0 as 16-byte
+ * reads of whole 1 KiB rows (16 KiB per wave and round), form 1 as the
+ * 8-byte transpose reads of the value products (ds_read_b64_tr_b16 at the
+ * prefill's swizzled offsets, 8 KiB per wave and round).  Each wave w writes
+ * its shader-clock cycles over the reads to cycles[w] (device, 8-byte
+ * aligned, workgroups * waves entries) and a fold of the data it read to
+ * sink[w] (device, 4-byte aligned, as many entries).  Asynchronous on
+ * `stream`.  Errors: PKV_ERR_BAD_SHAPE (sizes or form out of range),
+ * PKV_ERR_NULL_PTR, PKV_ERR_MISALIGNED, PKV_ERR_HIP.
+ */
+int pkv_lds_read_probe(uint64_t* cycles, uint32_t* sink, int32_t workgroups, int32_t waves,
+                       int32_t rounds, int32_t form, void* stream);
+
 /* Static description of a status code. */
 const char* pkv_status_string(int code);
 

@@ -545,6 +545,23 @@ def hbm_copy_probe(src, dst, workgroups=4096):
     _lib.check("pkv_hbm_copy_probe", code)
 
 
+def lds_read_probe(cycles, sink, workgroups, waves, rounds, form):
+    """Time LDS reads on every CU (measurement aid, see pkv_lds_read_probe):
+    ``cycles`` (int64) and ``sink`` (int32) are contiguous device tensors of
+    ``workgroups * waves`` entries; form 0 is 16-byte row reads, form 1 the
+    prefill's transpose reads."""
+    lib = _lib.load_library()
+    n = workgroups * waves
+    _need(cycles, "cycles", torch.int64, ndim=1)
+    _need(sink, "sink", torch.int32, cycles.device, ndim=1)
+    if cycles.numel() != n or sink.numel() != n:
+        raise ValueError("cycles and sink need workgroups * waves entries")
+    with torch.cuda.device(cycles.device):
+        code = lib.pkv_lds_read_probe(_ptr(cycles), _ptr(sink), workgroups, waves, rounds, form,
+                                      _stream_handle(cycles.device))
+    _lib.check("pkv_lds_read_probe", code)
+
+
 def hbm_gather_probe(buf, order, chunk_bytes, sink, workgroups=512):
     """Read ``buf`` as chunks of ``chunk_bytes`` in the order of ``order``
     (int32 device tensor, one entry per chunk); measurement aid, see

@@ -226,6 +226,15 @@ def test_probe_rejects_bad_arguments(lib):
     assert g(A16, 8192, A16, 4096, A16, 0, None) == _lib.ERR_BAD_SHAPE
     assert g(A16, 8192, None, 4096, A16, 64, None) == _lib.ERR_NULL_PTR
     assert g(A4, 8192, A16, 4096, A16, 64, None) == _lib.ERR_MISALIGNED
+    s = lib.pkv_lds_read_probe
+    assert s(A16, A16, 0, 4, 1, 0, None) == _lib.ERR_BAD_SHAPE
+    assert s(A16, A16, 8, 0, 1, 0, None) == _lib.ERR_BAD_SHAPE
+    assert s(A16, A16, 8, 17, 1, 0, None) == _lib.ERR_BAD_SHAPE
+    assert s(A16, A16, 8, 4, 0, 0, None) == _lib.ERR_BAD_SHAPE
+    assert s(A16, A16, 8, 4, 1, 2, None) == _lib.ERR_BAD_SHAPE
+    assert s(None, A16, 8, 4, 1, 0, None) == _lib.ERR_NULL_PTR
+    assert s(A16, None, 8, 4, 1, 0, None) == _lib.ERR_NULL_PTR
+    assert s(A4, A16, 8, 4, 1, 0, None) == _lib.ERR_MISALIGNED
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

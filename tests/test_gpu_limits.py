@@ -128,3 +128,41 @@ def test_copy_probe_copies_every_byte():
     torch.cuda.synchronize()
     assert torch.equal(dst[:n], src)
     assert not dst[n:].any()
+
+
+def test_lds_probe_reads_what_it_wrote():
+    """The LDS probe's 16-byte reads return the pattern it wrote (each
+    wave's fold equals the one computed here), its transpose reads give
+    the same fold on two runs, and every wave reports a positive cycle
+    count."""
+    from paged_kv_cache_03_amd.ops import lds_read_probe
+    G, W, R = 8, 4, 3
+    cycles = torch.zeros(G * W, dtype=torch.int64, device=dev())
+    sink = torch.zeros(G * W, dtype=torch.int32, device=dev())
+    print("lds probe, form 0", flush=True)
+    lds_read_probe(cycles, sink, G, W, R, 0)
+    torch.cuda.synchronize()
+    assert (cycles > 0).all()
+    # lane l of wave w reads unit i = ((r*16 + k + w) % 64) * 64 + l, which
+    # holds {i, 3i, i ^ 0x5555, i + 7}, and adds x ^ w = i ^ (i + 7); the
+    # wave's fold is lane 0's sum plus lane 1's (mod 2^32)
+    want = []
+    for w in range(W):
+        tot = 0
+        for lane in (0, 1):
+            for r in range(R):
+                for k in range(16):
+                    i = ((r * 16 + k + w) % 64) * 64 + lane
+                    tot += i ^ (i + 7)
+        want.append(tot % (1 << 32))
+    got = sink.cpu().numpy().astype(np.int64) % (1 << 32)
+    assert [int(x) for x in got.reshape(G, W)[0]] == want
+    assert (got.reshape(G, W) == got.reshape(G, W)[0]).all()
+    print("lds probe, form 1", flush=True)
+    lds_read_probe(cycles, sink, G, W, R, 1)
+    torch.cuda.synchronize()
+    first = sink.clone()
+    lds_read_probe(cycles, sink, G, W, R, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(first, sink) and (cycles > 0).all()
+
