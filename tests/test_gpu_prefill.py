@@ -125,6 +125,30 @@ def test_thousands_of_sequences_many_without_rows():
     assert_close(out, ref, "prefill over 5,000 sequences")
 
 
+def test_staging_at_the_lds_limit():
+    """A call whose group table and block ids fill the LDS staging to within
+    a few entries of its 32 KiB: 7,100 sequences (the group table) and one
+    16,000-token context (1,000 block ids, staged by the fill's second loop;
+    the pair read's spare entry is the allocation's last), with a few query
+    rows at its end and some in the first and last sequences."""
+    rng = np.random.default_rng(93)
+    B = 7100
+    lens = rng.integers(0, 17, size=B)
+    nq = np.minimum(lens, 1)
+    nq[rng.random(B) < 0.5] = 0
+    lens[3500], nq[3500] = 16000, 5
+    lens[0], nq[0] = 16, 16
+    lens[-1], nq[-1] = 9, 9
+    max_ctx = 16000
+    blocks = -(-max_ctx // 16)
+    assert ((((B + 2) & ~1) + blocks + 1) * 4) <= 32 * 1024
+    q, kp, vp, tables, lens, qs = _ragged(93, 2, 64, list(lens), list(nq))
+    scale = float(np.float32(64 ** -0.5))
+    out = run_prefill(q, to_dev(kp), to_dev(vp), tables, lens, qs, scale, max_ctx)
+    ref = paged_prefill_ref(q, kp, vp, tables, lens, qs, scale)
+    assert_close(out, ref, "prefill at the LDS staging limit")
+
+
 @pytest.mark.parametrize("mult", [1.0, -1.0, 0.0, 4.0])
 def test_scale_sign_zero_and_rising_scores(mult):
     """Keys that grow along the sequence (scores rise, so the online
