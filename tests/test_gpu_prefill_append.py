@@ -202,3 +202,22 @@ def test_new_token_blocks_outside_the_pool_are_not_written(D):
     assert torch.equal(out_f[rows], out_s[rows])
     ref = paged_prefill_ref(q, k_ref, v_ref, tables, lens, qs, scale, seqs=good)
     assert_close(out_f, ref, f"fused prefill, entries outside the pool, D={D}")
+
+
+def test_staging_at_the_lds_limit():
+    """The fused call with its LDS staging within a few entries of the
+    limit: 7,100 sequences and one 16,000-token context (1,000 block ids)
+    whose last 300 tokens are new (some of them in a block shared with
+    cached tokens), besides thousands of short prompts and chunks."""
+    rng = np.random.default_rng(95)
+    B = 7100
+    lens = rng.integers(0, 17, size=B)
+    nq = np.minimum(lens, rng.integers(0, 3, size=B))
+    lens[3500], nq[3500] = 16000, 300
+    lens[0], nq[0] = 16, 16
+    lens[-1], nq[-1] = 9, 9
+    assert ((((B + 2) & ~1) + 1000 + 1) * 4) <= 32 * 1024
+    q, k_new, v_new, kp, vp, tables, lens, qs = _case(95, 2, 64, list(lens), list(nq))
+    _check(q, k_new, v_new, kp, vp, tables, lens, qs, float(np.float32(64 ** -0.5)),
+           "fused prefill at the LDS staging limit")
+
